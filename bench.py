@@ -1,0 +1,196 @@
+"""Benchmark of the Engram lookup hot path on one MI355X.
+
+One step = the whole path over one batch: engram_hash (48 addresses per
+token) then engram_gather_reduce (48 FP8 rows -> two fp32 vectors of 256 per
+token).  Workload: 1 sequence of 131,072 Zipf(1.1) ids over a 129,280-id
+vocabulary, 48 sub-tables x 2^24 rows x 256 B FP8 E4M3 (192 GiB) plus fp32
+row scales, resident in HBM and filled on the device from a seeded
+generator.  Inputs are resident before the timed region starts.
+
+Prints one JSON line.  Extra figures (roofline of the gather kernel, the CPU
+oracle timed on a bounded sample of the same workload) ride in that line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+BYTES_PER_TOKEN = {  # algorithmic bytes of engram_gather_reduce per token
+    "rows": 48 * 256, "scales": 48 * 4, "addresses": 48 * 4, "output": 2 * 256 * 4}
+GATHER_BYTES_PER_TOKEN = sum(BYTES_PER_TOKEN.values())  # 14,720
+HASH_BYTES_PER_TOKEN = 4 + 48 * 4  # id in, addresses out
+PMC_FILE = os.path.join(ROOT, "profiles", "gather_reduce_full_131072_pmc.json")
+GATHER_SRC = os.path.join(ROOT, "hashed_gram_memory_amd", "csrc", "gather_reduce.hip")
+
+
+def _log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _traffic(n_tok: int):
+    """HBM bytes per gather launch from the committed counter summary, if it matches the current kernel."""
+    try:
+        rec = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    src = hashlib.sha256(open(GATHER_SRC, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != src or rec.get("n_tok") != n_tok:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(ids, rows: int, seed: int, sample_tokens: int):
+    """The CPU oracle on the first ``sample_tokens`` tokens of the workload, full-size tables."""
+    import oracle
+    import workloads
+
+    sub_ids = np.ascontiguousarray(ids[:, :sample_tokens])
+    mult = oracle.multipliers()
+    addr = oracle.hash_addresses(oracle.windows(sub_ids), mult, [rows] * 48)
+    host = workloads.SparseHostTables(seed, rows)
+    try:
+        host.materialise(addr)  # input preparation, untimed
+        t0 = time.perf_counter()
+        a = oracle.hash_addresses(oracle.windows(sub_ids), mult, [rows] * 48)
+        oracle.gather_reduce(host.tables, host.scales, a)
+        dt = time.perf_counter() - t0
+    finally:
+        host.close()
+    return {
+        "value": sample_tokens / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first {sample_tokens} tokens of the same 131072-token Zipf stream: oracle windows + hash + "
+                   f"gather-reduce (numpy, float64) against full-size 48 x 2^{rows.bit_length() - 1} host tables "
+                   f"(only touched rows resident); {dt:.1f} s"),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-sample", type=int, default=32768, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--id-batches", type=int, default=1,
+                    help="rotate among this many seeded id batches of the same shape (1: the workload's own ids)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the lookup needs no collective and this build runs on a "
+              "single MI355X; multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import hashed_gram_memory_amd as hg
+    import workloads
+
+    w = workloads.WORKLOADS[4]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n_tok = w.n_tok
+
+    _log(f"allocating 48 x {w.rows} x 256 B tables")
+    tables = torch.empty((48, w.rows, 256), dtype=torch.uint8, device=dev)
+    scales = torch.empty((48, w.rows), dtype=torch.float32, device=dev)
+    hg.synth_fill(tables, scales, w.table_seed)
+    torch.cuda.synchronize()
+    plan = hg.Plan(tables, scales)
+
+    batches = []
+    for b in range(args.id_batches):
+        ids, _ = workloads.make_ids(w, None if b == 0 else w.token_seed + 100 * b)
+        batches.append((ids, torch.from_numpy(ids).to(dev)))
+    addr = torch.empty((n_tok, 48), dtype=torch.uint32, device=dev)
+    out = torch.empty((n_tok, 2, 256), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        hg.hash(plan, batches[i % len(batches)][1], None, out=addr, stream=stream)
+        hg.gather_reduce(plan, addr, out=out, stream=stream)
+
+    _log(f"warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    _log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        hg.hash(plan, batches[i % len(batches)][1], None, out=addr, stream=stream)
+        e[1].record(stream)
+        hg.gather_reduce(plan, addr, out=out, stream=stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    hash_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    gather_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = wall / args.steps * 1e3
+    tok_s = n_tok / (ms_per_step / 1e3)
+    achieved = GATHER_BYTES_PER_TOKEN * n_tok / (gather_ms / 1e3) / 1e9
+    traffic = _traffic(n_tok)
+
+    base = None
+    if args.cpu_sample > 0:
+        _log(f"cpu baseline: oracle on {args.cpu_sample} tokens")
+        base = cpu_baseline(batches[0][0], w.rows, w.table_seed, min(args.cpu_sample, n_tok))
+
+    rec = {
+        "metric": "Engram lookup tokens/sec and achieved gather HBM GB/s (% of peak), 1 MI355X",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("full-size prefill: 1 x 131072 Zipf(1.1) ids over 129280; 48 sub-tables x 2^24 rows x 256 B "
+                         "FP8 E4M3 (192 GiB) + fp32 row scales, resident in HBM"),
+            "n_tok": n_tok,
+            "rows_per_subtable": w.rows,
+            "id_batches": args.id_batches,
+            "step": "engram_hash + engram_gather_reduce",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gather_reduce_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+        },
+        "gather_ms": gather_ms,
+        "hash_ms": hash_ms,
+        "hash_gbps": HASH_BYTES_PER_TOKEN * n_tok / (hash_ms / 1e3) / 1e9,
+        "gather_bytes_per_token": GATHER_BYTES_PER_TOKEN,
+        "cpu_baseline": base,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,294 @@
+"""Python binding of libengram.so, the Engram n-gram memory lookup for MI355X.
+
+Argument marshalling only: every step of the lookup runs in the library's
+HIP kernels.  PyTorch provides device memory and streams.  The library must
+be built (``python -m hashed_gram_memory_amd.build``); importing this package
+without it raises ImportError -- there is no fallback path.
+
+Functions mirror the C ABI in include/engram.h:
+
+    plan = Plan(tables, scales)                 # engram_plan
+    addr = hash(plan, ids, history)             # engram_hash
+    out  = gather_reduce(plan, addr)            # engram_gather_reduce
+    groups = dedup(plan, ids, history)          # engram_dedup
+    out  = gather_reduce(plan, addr, groups=groups)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # loads the process's HIP runtime before the library binds to it
+
+N_MODULES = 2
+N_SUB = 48
+ROW_BYTES = 256
+N_MULT = 192
+DEFAULT_HASH_SEED = 0x454E4752414D0001
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libengram.so")
+
+STATUS = {0: "ENGRAM_OK", -1: "ENGRAM_EINVAL", -2: "ENGRAM_ERANGE", -3: "ENGRAM_EWORKSPACE",
+          -4: "ENGRAM_EHIP", -5: "ENGRAM_EUNSUPPORTED"}
+
+
+class EngramError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_lib.engram_status_string(status).decode()} ({status})")
+
+
+class PlanDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_modules", ctypes.c_uint32),
+        ("min_order", ctypes.c_uint32),
+        ("max_order", ctypes.c_uint32),
+        ("n_heads", ctypes.c_uint32),
+        ("row_bytes", ctypes.c_uint32),
+        ("reserved0", ctypes.c_uint32),
+        ("hash_seed", ctypes.c_uint64),
+        ("rows", ctypes.POINTER(ctypes.c_uint64)),
+        ("tables", ctypes.POINTER(ctypes.c_void_p)),
+        ("scales", ctypes.POINTER(ctypes.c_void_p)),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m hashed_gram_memory_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, U64, U32, VP = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p
+    sig = {
+        "engram_plan_desc_init": [ctypes.POINTER(PlanDesc)],
+        "engram_plan": [ctypes.POINTER(PlanDesc), ctypes.POINTER(P)],
+        "engram_plan_destroy": [P],
+        "engram_plan_multipliers": [P, ctypes.POINTER(ctypes.c_uint64)],
+        "engram_hash": [P, VP, VP, I64, I64, VP, VP],
+        "engram_gather_reduce": [P, VP, I64, VP, VP, VP, VP, VP],
+        "engram_dedup_workspace": [I64, ctypes.POINTER(ctypes.c_size_t)],
+        "engram_dedup": [P, VP, VP, I64, I64, VP, VP, VP, VP, ctypes.c_size_t, VP],
+        "engram_synth_fill": [VP, VP, U64, U32, U64, VP],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.engram_status_string.argtypes = [ctypes.c_int]
+    lib.engram_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise EngramError(status, what)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream or None
+    return int(stream) or None
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+class Plan:
+    """An immutable lookup plan over 48 device sub-tables.
+
+    ``tables``: one uint8 tensor [48, R, 256] or a list of 48 tensors
+    [R_s, 256]; ``scales``: float32 [48, R] or a list of 48 tensors [R_s].
+    The tensors are referenced (not copied) and kept alive by the plan.
+    """
+
+    def __init__(self, tables, scales, hash_seed: int = DEFAULT_HASH_SEED):
+        if isinstance(tables, torch.Tensor):
+            if tables.dim() != 3 or tables.shape[0] != N_SUB or tables.shape[2] != ROW_BYTES:
+                raise ValueError("tables must be [48, R, 256]")
+            tables = list(tables.unbind(0))
+        if isinstance(scales, torch.Tensor):
+            if scales.dim() != 2 or scales.shape[0] != N_SUB:
+                raise ValueError("scales must be [48, R]")
+            scales = list(scales.unbind(0))
+        if len(tables) != N_SUB or len(scales) != N_SUB:
+            raise ValueError("need 48 tables and 48 scale vectors")
+        rows = []
+        for s in range(N_SUB):
+            t, c = tables[s], scales[s]
+            if t.dim() != 2 or t.shape[1] != ROW_BYTES or c.dim() != 1 or c.shape[0] != t.shape[0]:
+                raise ValueError(f"sub-table {s}: need table [R, 256] and scales [R]")
+            _dev(t, torch.uint8, f"tables[{s}]")
+            _dev(c, torch.float32, f"scales[{s}]")
+            rows.append(t.shape[0])
+        self._build(rows, [t.data_ptr() for t in tables], [c.data_ptr() for c in scales], hash_seed,
+                    keep=(tables, scales))
+
+    @classmethod
+    def from_pointers(cls, rows, table_ptrs, scale_ptrs, hash_seed: int = DEFAULT_HASH_SEED, keep=None) -> "Plan":
+        """Plan over raw device pointers (48 each) with the given row counts; ``keep`` is held alive."""
+        p = cls.__new__(cls)
+        p._build(list(rows), list(table_ptrs), list(scale_ptrs), hash_seed, keep)
+        return p
+
+    def _build(self, rows, tab_ptrs, sc_ptrs, hash_seed, keep) -> None:
+        if len(rows) != N_SUB or len(tab_ptrs) != N_SUB or len(sc_ptrs) != N_SUB:
+            raise ValueError("need 48 row counts, table pointers and scale pointers")
+        self._handle = None
+        self.rows = rows
+        self.hash_seed = hash_seed
+        self._keep = keep
+        self._rows_c = (ctypes.c_uint64 * N_SUB)(*rows)
+        self._tabs_c = (ctypes.c_void_p * N_SUB)(*tab_ptrs)
+        self._scs_c = (ctypes.c_void_p * N_SUB)(*sc_ptrs)
+        desc = PlanDesc()
+        _check(_lib.engram_plan_desc_init(ctypes.byref(desc)), "engram_plan_desc_init")
+        desc.hash_seed = hash_seed
+        desc.rows = ctypes.cast(self._rows_c, ctypes.POINTER(ctypes.c_uint64))
+        desc.tables = ctypes.cast(self._tabs_c, ctypes.POINTER(ctypes.c_void_p))
+        desc.scales = ctypes.cast(self._scs_c, ctypes.POINTER(ctypes.c_void_p))
+        handle = ctypes.c_void_p()
+        _check(_lib.engram_plan(ctypes.byref(desc), ctypes.byref(handle)), "engram_plan")
+        self._handle = handle
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._handle
+
+    def multipliers(self) -> list[int]:
+        buf = (ctypes.c_uint64 * N_MULT)()
+        _check(_lib.engram_plan_multipliers(self._handle, buf), "engram_plan_multipliers")
+        return list(buf)
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None):
+            _lib.engram_plan_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ids_shape(ids: torch.Tensor, history):
+    if ids.dim() != 2:
+        raise ValueError("ids must be [n_seq, seq_len]")
+    n_seq, seq_len = ids.shape
+    if history is not None and tuple(history.shape) != (n_seq, 3):
+        raise ValueError("history must be [n_seq, 3]")
+    return n_seq, seq_len
+
+
+def hash(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, out: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
+    """48 row addresses per token: uint32 [n_seq*seq_len, 48] (engram_hash)."""
+    n_seq, seq_len = _ids_shape(ids, history)
+    n_tok = n_seq * seq_len
+    if out is None:
+        out = torch.empty((n_tok, N_SUB), dtype=torch.uint32, device=ids.device)
+    elif tuple(out.shape) != (n_tok, N_SUB):
+        raise ValueError("out must be [n_tok, 48]")
+    st = _lib.engram_hash(plan.handle, _dev(ids, torch.int32, "ids"),
+                          None if history is None else _dev(history, torch.int32, "history"),
+                          n_seq, seq_len, _dev(out, torch.uint32, "addr"), _stream(stream))
+    _check(st, "engram_hash")
+    return out
+
+
+@dataclass
+class Groups:
+    """Result of dedup: device perm [n_tok], offsets [n_tok+1], n_unique [1]."""
+
+    perm: torch.Tensor
+    offsets: torch.Tensor
+    n_unique: torch.Tensor
+
+
+def gather_reduce(plan: Plan, addr: torch.Tensor, out: torch.Tensor | None = None, groups: Groups | None = None,
+                  stream=None) -> torch.Tensor:
+    """Per-module sum of the 24 dequantised rows: fp32 [n_tok, 2, 256] (engram_gather_reduce)."""
+    if addr.dim() != 2 or addr.shape[1] != N_SUB:
+        raise ValueError("addr must be [n_tok, 48]")
+    n_tok = addr.shape[0]
+    if out is None:
+        out = torch.empty((n_tok, N_MODULES, ROW_BYTES), dtype=torch.float32, device=addr.device)
+    elif tuple(out.shape) != (n_tok, N_MODULES, ROW_BYTES):
+        raise ValueError("out must be [n_tok, 2, 256]")
+    perm = offsets = n_unique = None
+    if groups is not None:
+        if groups.perm.shape[0] != n_tok or groups.offsets.shape[0] != n_tok + 1:
+            raise ValueError("groups do not match addr")
+        perm = _dev(groups.perm, torch.int32, "perm")
+        offsets = _dev(groups.offsets, torch.int32, "offsets")
+        n_unique = _dev(groups.n_unique, torch.int32, "n_unique")
+    st = _lib.engram_gather_reduce(plan.handle, _dev(addr, torch.uint32, "addr"), n_tok, perm, offsets, n_unique,
+                                   _dev(out, torch.float32, "out"), _stream(stream))
+    _check(st, "engram_gather_reduce")
+    return out
+
+
+def dedup_workspace_bytes(n_tok: int) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.engram_dedup_workspace(n_tok, ctypes.byref(b)), "engram_dedup_workspace")
+    return b.value
+
+
+def dedup(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+          groups: Groups | None = None, stream=None) -> Groups:
+    """Group tokens with equal id windows (engram_dedup)."""
+    n_seq, seq_len = _ids_shape(ids, history)
+    n_tok = n_seq * seq_len
+    dev = ids.device
+    if groups is None:
+        groups = Groups(torch.empty(n_tok, dtype=torch.int32, device=dev),
+                        torch.empty(n_tok + 1, dtype=torch.int32, device=dev),
+                        torch.empty(1, dtype=torch.int32, device=dev))
+    need = dedup_workspace_bytes(n_tok)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = _lib.engram_dedup(plan.handle, _dev(ids, torch.int32, "ids"),
+                           None if history is None else _dev(history, torch.int32, "history"), n_seq, seq_len,
+                           _dev(groups.perm, torch.int32, "perm"), _dev(groups.offsets, torch.int32, "offsets"),
+                           _dev(groups.n_unique, torch.int32, "n_unique"), _dev(workspace, torch.uint8, "workspace"),
+                           workspace.numel(), _stream(stream))
+    _check(st, "engram_dedup")
+    return groups
+
+
+def synth_fill(tables, scales, seed: int, stream=None) -> None:
+    """Fill 48 sub-tables from the seeded generator (engram_synth_fill).
+
+    ``tables``: uint8 [48, R, 256] or a list of 48 [R, 256]; ``scales``:
+    float32 [48, R] or a list of 48 [R].
+    """
+    tables = list(tables.unbind(0)) if isinstance(tables, torch.Tensor) else list(tables)
+    scales = list(scales.unbind(0)) if isinstance(scales, torch.Tensor) else list(scales)
+    if len(tables) != N_SUB or len(scales) != N_SUB:
+        raise ValueError("need 48 tables and 48 scale vectors")
+    for s in range(N_SUB):
+        t, c = tables[s], scales[s]
+        if t.dim() != 2 or t.shape[1] != ROW_BYTES or tuple(c.shape) != (t.shape[0],):
+            raise ValueError(f"sub-table {s}: need table [R, 256] and scales [R]")
+        st = _lib.engram_synth_fill(_dev(t, torch.uint8, "table"), _dev(c, torch.float32, "scales"), t.shape[0], s,
+                                    seed, _stream(stream))
+        _check(st, "engram_synth_fill")

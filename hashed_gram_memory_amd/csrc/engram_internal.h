@@ -1,0 +1,55 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "engram.h"
+
+namespace engram {
+
+constexpr int kSub = ENGRAM_N_SUB;
+constexpr int kRowsPerModule = ENGRAM_ROWS_PER_MODULE;
+constexpr int kRowBytes = ENGRAM_ROW_BYTES;
+constexpr int kMult = ENGRAM_N_MULT;
+constexpr int64_t kMaxTokens = (int64_t(1) << 31) - 1;
+
+// Everything the hash kernel needs, passed by value (lands in the kernel
+// argument segment and is read with scalar loads).
+struct HashParams {
+    uint64_t mult[kMult];  // M[((m*3 + (n-2))*8 + h)*4 + k]
+    uint64_t rows[kSub];   // R_s
+    uint64_t magic[kSub];  // floor((2^64 - 1) / R_s): exact x mod R_s with one correction
+};
+
+// Row and scale base pointers of the 48 sub-tables, by value.
+struct GatherParams {
+    const uint8_t* tab[kSub];
+    const float* sc[kSub];
+};
+
+}  // namespace engram
+
+struct engram_plan_s {
+    uint64_t hash_seed;
+    engram::HashParams hash;
+    engram::GatherParams gather;
+};
+
+namespace engram {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+hipError_t launch_hash(const HashParams& p, const int32_t* ids, const int32_t* history,
+                       uint32_t n_tok, uint32_t seq_len, uint32_t* addr, hipStream_t stream);
+
+hipError_t launch_gather_reduce(const GatherParams& p, const uint32_t* addr, uint32_t n_tok,
+                                const int32_t* perm, const int32_t* offsets, const int32_t* n_unique,
+                                float* out, hipStream_t stream);
+
+size_t dedup_workspace_bytes(uint32_t n_tok);
+
+hipError_t launch_dedup(const int32_t* ids, const int32_t* history, uint32_t n_tok, uint32_t seq_len,
+                        int32_t* perm, int32_t* offsets, int32_t* n_unique, void* ws, hipStream_t stream);
+
+}  // namespace engram

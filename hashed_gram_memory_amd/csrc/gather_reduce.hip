@@ -1,0 +1,124 @@
+// Gather-reduce kernel: read 24 FP8 rows per (token, module), dequantise
+// with the per-row scale and sum them into one fp32 vector of 256.
+//
+// The pages: every token reads 48 rows of 256 FP8 bytes (two modules of 24)
+// [How to Run DeepSeek-V4.1-Flash: 510 GB, and 203 GB of It Is a Lookup
+// Table, section "Engram: the table that is never multiplied"; DeepSeek V4.1
+// Flash: The VRAM Killer, section "What makes up the 511 GB of weights?"];
+// the rows come from FP8 tables and are combined [Running DeepSeek V4.1
+// Flash locally: the numbers beyond 552B, section "Backbone, Engram, and
+// active parameters describe different scales"].  It is a lookup, not a
+// matrix product: HBM-bound random 256-byte reads, no MFMA.
+//
+// Mapping (gfx950, wave64):
+//   * one wavefront per (token, module); a row is one coalesced
+//     global_load_dword of 64 lanes x 4 B, lane l holding elements 4l..4l+3;
+//   * the 24 addresses of a (token, module) are contiguous and wave-uniform
+//     (scalar loads), as are the 24 row bases and the 24 scales;
+//   * all 24 row loads are issued before the first is consumed, so a wave
+//     keeps 24 x 256 B in flight; with up to 8 waves per SIMD that is
+//     ~200 KB in flight per CU;
+//   * decode with the gfx950 packed FP8 (OCP E4M3) -> fp32 conversion, then
+//     fused multiply-add into 4 fp32 accumulators per lane in ascending q;
+//   * the 1 KiB result is written with non-temporal stores so output
+//     traffic does not evict table rows from L2 / MALL;
+//   * XCD-aware block order: the dispatcher hands block b to XCD b % 8; the
+//     grid is laid out so XCDs 0-3 serve module 0 and XCDs 4-7 module 1,
+//     which halves the set of sub-tables each XCD's L2 has to cache.
+#include "engram_internal.h"
+
+namespace engram {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Sum of the 24 dequantised rows of module m (wave-uniform) for one token;
+// `a` points at the token's 48 addresses.
+__device__ __forceinline__ f32x4 module_sum(const GatherParams& P, const uint32_t* __restrict__ a, uint32_t m,
+                                            uint32_t lane) {
+    uint32_t v[kRowsPerModule];
+    float sc[kRowsPerModule];
+    const uint32_t s0 = m * kRowsPerModule;
+#pragma unroll
+    for (int q = 0; q < kRowsPerModule; ++q) {
+        const uint32_t r = a[s0 + q];
+        const uint32_t* row =
+            reinterpret_cast<const uint32_t*>(P.tab[s0 + q] + static_cast<uint64_t>(r) * kRowBytes);
+        v[q] = row[lane];
+        sc[q] = P.sc[s0 + q][r];
+    }
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < kRowsPerModule; ++q) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[q]), false);  // bytes 0, 1
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[q]), true);   // bytes 2, 3
+        acc.x = __builtin_fmaf(lo[0], sc[q], acc.x);
+        acc.y = __builtin_fmaf(lo[1], sc[q], acc.y);
+        acc.z = __builtin_fmaf(hi[0], sc[q], acc.z);
+        acc.w = __builtin_fmaf(hi[1], sc[q], acc.w);
+    }
+    return acc;
+}
+
+template <bool kDedup>
+__global__ __launch_bounds__(256) void gather_reduce_kernel(const GatherParams P, const uint32_t* __restrict__ addr,
+                                                            uint32_t item_base, uint32_t n_items,
+                                                            const int32_t* __restrict__ perm,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ n_unique,
+                                                            float* __restrict__ out) {
+    const uint32_t b = blockIdx.x;
+    const uint32_t xcd = b & 7u;
+    const uint32_t module = xcd >> 2;
+    const uint32_t group = (b >> 3) * 4u + (xcd & 3u);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t item = item_base + group * 4u + wave;
+
+    uint32_t limit = n_items;
+    if (kDedup) limit = min(limit, static_cast<uint32_t>(*n_unique));
+    if (item >= limit) return;
+
+    uint32_t tok = item;
+    if (kDedup) tok = static_cast<uint32_t>(perm[offsets[item]]);
+    const uint32_t* a = addr + static_cast<size_t>(tok) * kSub;
+    const f32x4 acc = module_sum(P, a, module, lane);
+
+    const size_t col = static_cast<size_t>(module) * kRowBytes + lane * 4u;
+    if (!kDedup) {
+        __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + col));
+    } else {
+        const int32_t end = offsets[item + 1];
+        for (int32_t i = offsets[item]; i < end; ++i) {
+            const uint32_t t = static_cast<uint32_t>(perm[i]);
+            __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(t) * (2 * kRowBytes) + col));
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gather_reduce(const GatherParams& p, const uint32_t* addr, uint32_t n_tok, const int32_t* perm,
+                                const int32_t* offsets, const int32_t* n_unique, float* out, hipStream_t stream) {
+    // 4 items (one per wave) per block and module; groups rounded up to a
+    // multiple of 4 so that every (group, module) maps to exactly one block.
+    // Launches cover at most 2^24 items so the grid stays far below 2^32
+    // threads.
+    constexpr uint32_t kChunk = 1u << 24;
+    for (uint32_t base = 0; base < n_tok; base += kChunk) {
+        const uint32_t n = min(kChunk, n_tok - base);
+        const uint32_t groups = ((n + 3u) / 4u + 3u) & ~3u;
+        const dim3 grid(2u * groups), block(256);
+        if (perm)
+            hipLaunchKernelGGL(gather_reduce_kernel<true>, grid, block, 0, stream, p, addr, base, base + n, perm,
+                               offsets, n_unique, out);
+        else
+            hipLaunchKernelGGL(gather_reduce_kernel<false>, grid, block, 0, stream, p, addr, base, base + n, perm,
+                               offsets, n_unique, out);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace engram

@@ -1,0 +1,211 @@
+/*
+ * engram.h -- C ABI of the Engram n-gram memory lookup for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [VRAM]  "DeepSeek V4.1 Flash: The VRAM Killer. Can You Run It Locally?",
+ *           section "What makes up the 511 GB of weights?"
+ *   [GUIDE] "How to Run DeepSeek-V4.1-Flash: 510 GB, and 203 GB of It Is a
+ *           Lookup Table", sections "The architecture", "Where the 510 GB
+ *           goes" and "Engram: the table that is never multiplied"
+ *   [REQ]   "Running DeepSeek V4.1 Flash locally: the numbers beyond 552B",
+ *           section "Backbone, Engram, and active parameters describe
+ *           different scales"
+ *
+ * The operation.  Two Engram modules each hash the suffix n-grams of order
+ * 2, 3 and 4 of the token-id stream with 8 independent heads and read one
+ * row per (order, head): 24 rows per module, 48 per token [GUIDE "Engram";
+ * VRAM].  Rows are 256 bytes of FP8 [GUIDE "Engram"; REQ]; each carries one
+ * fp32 scale here.  The row addresses depend on the token ids alone, so the
+ * whole prompt is hashed before any row is read [VRAM; GUIDE "Engram"]: the
+ * library exposes the hash and the gather as separate calls.  The 24
+ * dequantised rows of a module are summed into one fp32 vector of 256
+ * elements; the pages' learned gate that follows (row vs. hidden state,
+ * [GUIDE "The architecture"]) is not part of this library.
+ *
+ * Conventions for every call:
+ *   - Return value: ENGRAM_OK (0) or a negative engram_status.  No call
+ *     throws, aborts or prints.
+ *   - All arguments are validated on the host before anything is launched;
+ *     on an error return nothing has been launched and no output was
+ *     written.
+ *   - Calls that take a stream are asynchronous on that stream (a
+ *     hipStream_t passed as void*; NULL is the null stream).  They never
+ *     synchronise and never allocate device memory.
+ *   - Device pointers are owned by the caller and must stay valid until the
+ *     work queued on the stream has finished.
+ *   - Device-side faults (e.g. a table pointer that is not device memory)
+ *     surface at the caller's next synchronisation, as usual in HIP.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Geometry of the lookup [GUIDE "Engram"; VRAM]. */
+#define ENGRAM_N_MODULES 2        /* Engram modules (layers) per token           */
+#define ENGRAM_MIN_ORDER 2        /* shortest suffix n-gram                      */
+#define ENGRAM_MAX_ORDER 4        /* longest suffix n-gram, = id window length    */
+#define ENGRAM_N_HEADS 8          /* hash heads per (module, order)              */
+#define ENGRAM_ROWS_PER_MODULE 24 /* 3 orders x 8 heads                          */
+#define ENGRAM_N_SUB 48           /* sub-tables = rows read per token            */
+#define ENGRAM_ROW_BYTES 256      /* FP8 E4M3 codes per row = output width       */
+#define ENGRAM_N_MULT 192         /* hash multipliers: 2 x 3 x 8 x 4             */
+
+/* Seed of the default hash multipliers: the bytes "ENGRAM" followed by 0x0001. */
+#define ENGRAM_DEFAULT_HASH_SEED 0x454E4752414D0001ULL
+
+typedef enum engram_status {
+    ENGRAM_OK = 0,
+    ENGRAM_EINVAL = -1,      /* NULL or misaligned pointer, bad shape or flag       */
+    ENGRAM_ERANGE = -2,      /* row count 0 or > 2^32, token count out of range     */
+    ENGRAM_EWORKSPACE = -3,  /* workspace NULL or smaller than required             */
+    ENGRAM_EHIP = -4,        /* the HIP runtime refused a launch                    */
+    ENGRAM_EUNSUPPORTED = -5 /* a geometry other than the one above                 */
+} engram_status;
+
+/*
+ * Plan description.  Sub-table s = 24*m + 8*(n-2) + h holds module m, order
+ * n, head h (module-major, then order, then head).
+ *
+ *   n_modules, min_order, max_order, n_heads, row_bytes
+ *       Must equal 2, 2, 4, 8, 256 (else ENGRAM_EUNSUPPORTED).
+ *   hash_seed
+ *       Seeds the 192 hash multipliers: M[i] is output i+1 of splitmix64
+ *       (Steele, Lea and Flood 2014) seeded with hash_seed, with bit 0 set;
+ *       i runs over (module, order, head, k) in that nesting, k = 0..3.
+ *   rows[48]   (host array, copied)
+ *       Rows R_s of sub-table s, 1 <= R_s <= 2^32.
+ *   tables[48] (host array of device pointers, copied)
+ *       Sub-table s as row-major uint8 [R_s][256] of FP8 E4M3 codes (OCP
+ *       encoding: bias 7, no infinities, 0x7F/0xFF are NaN).  16-byte aligned.
+ *   scales[48] (host array of device pointers, copied)
+ *       fp32 [R_s]: the scale of each row.  4-byte aligned.
+ *
+ * The plan copies the description; the tables themselves are not copied and
+ * must outlive every call that uses the plan.
+ */
+typedef struct engram_plan_desc {
+    uint32_t n_modules;
+    uint32_t min_order;
+    uint32_t max_order;
+    uint32_t n_heads;
+    uint32_t row_bytes;
+    uint32_t reserved0;            /* must be 0 */
+    uint64_t hash_seed;
+    const uint64_t* rows;
+    const uint8_t* const* tables;
+    const float* const* scales;
+} engram_plan_desc;
+
+typedef struct engram_plan_s* engram_plan_t;
+
+/* Fill a description with the default geometry and hash seed; the caller
+ * still sets rows, tables and scales.  Returns ENGRAM_EINVAL on NULL. */
+int engram_plan_desc_init(engram_plan_desc* desc);
+
+/*
+ * Validate a description and build an immutable plan: copies the row counts
+ * and pointers, derives the multipliers and the exact division constants of
+ * each R_s.  Host-only: touches no device and may run before any device
+ * exists.  *out is set only on ENGRAM_OK.  A plan may be used from several
+ * host threads and streams at once.
+ */
+int engram_plan(const engram_plan_desc* desc, engram_plan_t* out);
+
+/* Release a plan (NULL is accepted).  No work using it may be in flight. */
+int engram_plan_destroy(engram_plan_t plan);
+
+/* Copy the 192 hash multipliers of a plan into host memory out[192], in
+ * (module, order, head, k) order. */
+int engram_plan_multipliers(engram_plan_t plan, uint64_t* out);
+
+/*
+ * Hash: 48 row addresses per token [GUIDE "Engram"; VRAM].
+ *
+ * Token tok = s*seq_len + t has the id window w_k = id at position t-k,
+ * k = 0..3; positions before 0 read history[s][3 + (t-k)] (history[s][2] is
+ * the id just before position 0) or, with history == NULL, id 0.  For
+ * module m, order n, head h, with u64 the zero-extension of the 32-bit id:
+ *     x = XOR_{k<n} ( u64(w_k) * M[m][n][h][k] )   (mod 2^64)
+ *     addr[tok][24*m + 8*(n-2) + h] = x mod R_s
+ *
+ *   ids      device int32 [n_seq][seq_len], ids in [0, 2^31); not checked on
+ *            the device (a negative id is a contract violation).
+ *   history  device int32 [n_seq][3] or NULL.
+ *   addr     device uint32 [n_seq*seq_len][48], 16-byte aligned (output).
+ *
+ * n_seq*seq_len == 0 is a no-op.  Errors: EINVAL (NULL/misaligned pointer,
+ * negative sizes), ERANGE (n_seq*seq_len >= 2^31).
+ */
+int engram_hash(engram_plan_t plan, const int32_t* ids, const int32_t* history,
+                int64_t n_seq, int64_t seq_len, uint32_t* addr, void* stream);
+
+/*
+ * Gather, dequantise and sum [GUIDE "Engram"; REQ].
+ *
+ * For token tok, module m and element j:
+ *     out[tok][m][j] = sum_{q=0..23} fp8(T_{24m+q}[a][j]) * scale_{24m+q}[a],
+ *     a = addr[tok][24m+q]
+ * accumulated in fp32 in ascending q (fused multiply-add), starting at +0.
+ *
+ *   addr    device uint32 [n_tok][48] (as written by engram_hash); every
+ *           address must be < R_s (not checked on the device).
+ *   out     device fp32 [n_tok][2][256], 16-byte aligned (output).
+ *
+ * Direct mode: perm, offsets and n_unique all NULL.
+ * Dedup mode: perm, offsets, n_unique as written by engram_dedup for the
+ * same tokens; each group of tokens with equal windows is looked up once
+ * and its vector stored to every member.  The result is bitwise identical
+ * to direct mode.  In dedup mode the grid covers n_tok groups and exits
+ * early past *n_unique, which stays on the device.
+ *
+ * n_tok == 0 is a no-op.  Errors: EINVAL (NULL/misaligned pointer, a partial
+ * set of dedup pointers), ERANGE (n_tok < 0 or >= 2^31).
+ */
+int engram_gather_reduce(engram_plan_t plan, const uint32_t* addr, int64_t n_tok,
+                         const int32_t* perm, const int32_t* offsets,
+                         const int32_t* n_unique, float* out, void* stream);
+
+/*
+ * Workspace bytes engram_dedup needs for n_tok tokens (host-only).
+ */
+int engram_dedup_workspace(int64_t n_tok, size_t* bytes);
+
+/*
+ * Group the tokens whose id windows (w_0, w_1, w_2, w_3) are equal: they
+ * hash to the same 48 rows, so one lookup serves the whole group.  This
+ * serves batches of prompts that share a prefix.  Groups are ordered by
+ * ascending window (w_0 most significant, ids compared as unsigned), tokens
+ * within a group by ascending index: the result is unique.
+ *
+ *   ids, history, n_seq, seq_len   as for engram_hash.
+ *   perm      device int32 [n_tok]: the tokens, group by group (output).
+ *   offsets   device int32 [n_tok + 1]: offsets[u] is where group u starts
+ *             in perm; offsets[n_unique] = n_tok; entries past n_unique are
+ *             left unspecified (output).
+ *   n_unique  device int32 [1]: the number of groups (output).
+ *   ws        device workspace of ws_bytes >= engram_dedup_workspace(n_tok),
+ *             256-byte aligned, owned by the caller, reusable after the
+ *             stream passes this call.
+ *
+ * n_tok == 0 writes offsets[0] = 0 and *n_unique = 0.  Errors: EINVAL,
+ * ERANGE, EWORKSPACE.
+ */
+int engram_dedup(engram_plan_t plan, const int32_t* ids, const int32_t* history,
+                 int64_t n_seq, int64_t seq_len, int32_t* perm, int32_t* offsets,
+                 int32_t* n_unique, void* ws, size_t ws_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* engram_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

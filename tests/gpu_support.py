@@ -1,0 +1,110 @@
+"""Helpers shared by the GPU parity tests (device tables, oracle on samples)."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+FULL_ROWS = 1 << 24
+
+
+def lib():
+    import hashed_gram_memory_amd as hg
+    return hg
+
+
+@functools.lru_cache(maxsize=1)
+def big_buffer():
+    """One [48, 2^24, 256] code buffer and [48, 2^24] scales (195 GiB), shared by all tests.
+
+    Smaller tables are views of its leading rows, one contiguous [R, 256]
+    block per sub-table.
+    """
+    tabs = torch.empty((48, FULL_ROWS, 256), dtype=torch.uint8, device="cuda")
+    scs = torch.empty((48, FULL_ROWS), dtype=torch.float32, device="cuda")
+    return tabs, scs
+
+
+_filled = {"key": None}
+
+
+def device_tables(rows: int, seed: int):
+    """48 device sub-tables of ``rows`` rows filled from the seeded generator (lists of views)."""
+    tabs, scs = big_buffer()
+    t = [tabs[s, :rows] for s in range(48)]
+    c = [scs[s, :rows] for s in range(48)]
+    if _filled["key"] != (rows, seed):
+        lib().synth_fill(t, c, seed)
+        torch.cuda.synchronize()
+        _filled["key"] = (rows, seed)
+    return t, c
+
+
+def mark_buffer_dirty():
+    _filled["key"] = None
+
+
+def small_device_tables(host_tabs, host_scs):
+    t = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in host_tabs]
+    c = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in host_scs]
+    return t, c
+
+
+def dummy_plan(rows: int):
+    """A plan whose tables are never read (hash-only tests): every pointer is one small buffer."""
+    t = torch.zeros((1, 256), dtype=torch.uint8, device="cuda")
+    c = torch.zeros(1, dtype=torch.float32, device="cuda")
+    return lib().Plan.from_pointers([rows] * 48, [t.data_ptr()] * 48, [c.data_ptr()] * 48, keep=(t, c))
+
+
+def to_dev_ids(ids, history):
+    d_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    d_hist = None if history is None else torch.from_numpy(np.ascontiguousarray(history, dtype=np.int32)).cuda()
+    return d_ids, d_hist
+
+
+def addr_to_host(addr: torch.Tensor) -> np.ndarray:
+    return addr.view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+def sample_tokens(n_tok: int, k: int, seed: int, must=()) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    pick = set(int(t) for t in must if 0 <= t < n_tok)
+    pick.update(range(min(4, n_tok)))
+    pick.add(n_tok - 1)
+    if n_tok > k:
+        pick.update(rng.choice(n_tok, size=k - len(pick), replace=False).tolist())
+    else:
+        pick.update(range(n_tok))
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def oracle_sampled(ids, history, rows: int, seed: int, tokens: np.ndarray):
+    """Oracle addresses for all tokens and memory vectors for ``tokens`` (regenerated rows)."""
+    addr = oracle.hash_addresses(oracle.windows(ids, history), oracle.multipliers(), [rows] * 48)
+    sub = addr[tokens]
+    host = workloads.SparseHostTables(seed, rows)
+    try:
+        host.materialise(sub)
+        out, abs_sum = oracle.gather_reduce(host.tables, host.scales, sub)
+    finally:
+        host.close()
+    return addr, out, abs_sum
+
+
+def assert_within_tolerance(gpu: np.ndarray, ref: np.ndarray, abs_sum: np.ndarray, rel: float = 1e-5):
+    """|gpu - ref| <= rel * sum|terms| per element; exact where the bound is 0; NaN where ref is NaN."""
+    gpu = gpu.astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(gpu), nan), "NaN positions differ"
+    ok = ~nan
+    err = np.abs(gpu[ok] - ref[ok])
+    bound = rel * abs_sum[ok]
+    bad = err > bound
+    if bad.any():
+        i = np.flatnonzero(bad)[:5]
+        raise AssertionError(f"{bad.sum()} elements out of tolerance; first: err={err[i]} bound={bound[i]}")

@@ -1,0 +1,204 @@
+"""The C ABI on the host: exported symbols, validation, plans (no device work)."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, EINVAL, ERANGE, EWORKSPACE, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced: validation fails or no launch happens
+
+
+@pytest.fixture(scope="module")
+def hg():
+    import hashed_gram_memory_amd as hg
+    return hg
+
+
+@pytest.fixture(scope="module")
+def L(hg):
+    return hg.lib()
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(engram_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _desc(hg, rows=None, tabs=None, scs=None):
+    d = hg.PlanDesc()
+    assert hg.lib().engram_plan_desc_init(ctypes.byref(d)) == OK
+    rows = rows if rows is not None else [4096] * 48
+    tabs = tabs if tabs is not None else [FAKE + 256 * s for s in range(48)]
+    scs = scs if scs is not None else [FAKE + 4 * s for s in range(48)]
+    keep = ((ctypes.c_uint64 * 48)(*rows), (ctypes.c_void_p * 48)(*tabs), (ctypes.c_void_p * 48)(*scs))
+    d.rows = ctypes.cast(keep[0], ctypes.POINTER(ctypes.c_uint64))
+    d.tables = ctypes.cast(keep[1], ctypes.POINTER(ctypes.c_void_p))
+    d.scales = ctypes.cast(keep[2], ctypes.POINTER(ctypes.c_void_p))
+    return d, keep
+
+
+def _plan(hg, d):
+    h = ctypes.c_void_p()
+    st = hg.lib().engram_plan(ctypes.byref(d), ctypes.byref(h))
+    return st, h
+
+
+def test_desc_init_defaults(hg):
+    d, _ = _desc(hg)
+    assert (d.n_modules, d.min_order, d.max_order, d.n_heads, d.row_bytes) == (2, 2, 4, 8, 256)
+    assert d.hash_seed == oracle.DEFAULT_HASH_SEED
+    assert hg.lib().engram_plan_desc_init(None) == EINVAL
+
+
+def test_plan_validation(hg):
+    L = hg.lib()
+    d, keep = _desc(hg)
+    st, h = _plan(hg, d)
+    assert st == OK and h.value
+    assert L.engram_plan_destroy(h) == OK
+    assert L.engram_plan_destroy(None) == OK
+    assert L.engram_plan(None, ctypes.byref(ctypes.c_void_p())) == EINVAL
+    assert L.engram_plan(ctypes.byref(d), None) == EINVAL
+    for field, val in (("n_modules", 1), ("min_order", 1), ("max_order", 5), ("n_heads", 4), ("row_bytes", 128)):
+        d2, k2 = _desc(hg)
+        setattr(d2, field, val)
+        assert _plan(hg, d2)[0] == EUNSUPPORTED, field
+    d2, k2 = _desc(hg)
+    d2.reserved0 = 1
+    assert _plan(hg, d2)[0] == EINVAL
+    for rows, want in (([0] * 48, ERANGE), ([(1 << 32) + 1] * 48, ERANGE), ([1 << 32] * 48, OK), ([1] * 48, OK)):
+        d2, k2 = _desc(hg, rows=rows)
+        st, h = _plan(hg, d2)
+        assert st == want, rows[0]
+        if st == OK:
+            L.engram_plan_destroy(h)
+    tabs = [FAKE] * 48
+    tabs[7] = FAKE + 8  # not 16-byte aligned
+    assert _plan(hg, _desc(hg, tabs=tabs)[0])[0] == EINVAL
+    tabs[7] = 0
+    assert _plan(hg, _desc(hg, tabs=tabs)[0])[0] == EINVAL
+    scs = [FAKE] * 48
+    scs[3] = FAKE + 2
+    assert _plan(hg, _desc(hg, scs=scs)[0])[0] == EINVAL
+    d2, k2 = _desc(hg)
+    d2.rows = None
+    assert _plan(hg, d2)[0] == EINVAL
+
+
+def test_plan_multipliers_match_oracle(hg):
+    """The library's host-side splitmix64 derivation agrees with the oracle's (independent code)."""
+    for seed in (oracle.DEFAULT_HASH_SEED, 0, 1234567, (1 << 64) - 1):
+        d, keep = _desc(hg)
+        d.hash_seed = seed
+        st, h = _plan(hg, d)
+        assert st == OK
+        buf = (ctypes.c_uint64 * 192)()
+        assert hg.lib().engram_plan_multipliers(h, buf) == OK
+        assert list(buf) == [int(v) for v in oracle.multipliers(seed).ravel()]
+        hg.lib().engram_plan_destroy(h)
+
+
+@pytest.fixture()
+def plan(hg):
+    d, keep = _desc(hg)
+    st, h = _plan(hg, d)
+    assert st == OK
+    yield h
+    hg.lib().engram_plan_destroy(h)
+
+
+def test_hash_validation(hg, plan):
+    L = hg.lib()
+    assert L.engram_hash(None, FAKE, None, 1, 1, FAKE, None) == EINVAL
+    assert L.engram_hash(plan, FAKE, None, 0, 100, FAKE, None) == OK  # no tokens: no launch
+    assert L.engram_hash(plan, None, None, 0, 0, None, None) == OK
+    assert L.engram_hash(plan, FAKE, None, -1, 4, FAKE, None) == EINVAL
+    assert L.engram_hash(plan, FAKE, None, 4, -1, FAKE, None) == EINVAL
+    assert L.engram_hash(plan, FAKE, None, 1 << 16, 1 << 15, FAKE, None) == ERANGE  # 2^31 tokens
+    assert L.engram_hash(plan, None, None, 1, 1, FAKE, None) == EINVAL
+    assert L.engram_hash(plan, FAKE, None, 1, 1, None, None) == EINVAL
+    assert L.engram_hash(plan, FAKE + 2, None, 1, 1, FAKE, None) == EINVAL
+    assert L.engram_hash(plan, FAKE, None, 1, 1, FAKE + 4, None) == EINVAL
+    assert L.engram_hash(plan, FAKE, FAKE + 1, 1, 1, FAKE, None) == EINVAL
+
+
+def test_gather_reduce_validation(hg, plan):
+    L = hg.lib()
+    assert L.engram_gather_reduce(None, FAKE, 1, None, None, None, FAKE, None) == EINVAL
+    assert L.engram_gather_reduce(plan, FAKE, 0, None, None, None, FAKE, None) == OK
+    assert L.engram_gather_reduce(plan, FAKE, -1, None, None, None, FAKE, None) == ERANGE
+    assert L.engram_gather_reduce(plan, FAKE, 1 << 31, None, None, None, FAKE, None) == ERANGE
+    assert L.engram_gather_reduce(plan, None, 1, None, None, None, FAKE, None) == EINVAL
+    assert L.engram_gather_reduce(plan, FAKE, 1, None, None, None, None, None) == EINVAL
+    assert L.engram_gather_reduce(plan, FAKE + 4, 1, None, None, None, FAKE, None) == EINVAL
+    assert L.engram_gather_reduce(plan, FAKE, 1, None, None, None, FAKE + 8, None) == EINVAL
+    assert L.engram_gather_reduce(plan, FAKE, 1, FAKE, None, None, FAKE, None) == EINVAL
+    assert L.engram_gather_reduce(plan, FAKE, 1, FAKE, FAKE, None, FAKE, None) == EINVAL
+    assert L.engram_gather_reduce(plan, FAKE, 1, FAKE + 1, FAKE, FAKE, FAKE, None) == EINVAL
+
+
+def test_dedup_validation(hg, plan):
+    L = hg.lib()
+    b = ctypes.c_size_t()
+    assert L.engram_dedup_workspace(-1, ctypes.byref(b)) == ERANGE
+    assert L.engram_dedup_workspace(1, None) == EINVAL
+    assert L.engram_dedup_workspace(1000, ctypes.byref(b)) == OK
+    need = b.value
+    if need:
+        assert L.engram_dedup(plan, FAKE, None, 1, 1000, FAKE, FAKE, FAKE, None, need, None) == EWORKSPACE
+        assert L.engram_dedup(plan, FAKE, None, 1, 1000, FAKE, FAKE, FAKE, FAKE, need - 1, None) == EWORKSPACE
+        assert L.engram_dedup(plan, FAKE, None, 1, 1000, FAKE, FAKE, FAKE, FAKE + 64, need, None) == EWORKSPACE
+    assert L.engram_dedup(plan, FAKE, None, 1, 1000, None, FAKE, FAKE, FAKE, need, None) == EINVAL
+    assert L.engram_dedup(plan, FAKE, None, 1, 1000, FAKE, None, FAKE, FAKE, need, None) == EINVAL
+    assert L.engram_dedup(plan, FAKE, None, 1, 1000, FAKE, FAKE, None, FAKE, need, None) == EINVAL
+    assert L.engram_dedup(plan, FAKE, None, -1, 1000, FAKE, FAKE, FAKE, FAKE, need, None) == EINVAL
+    assert L.engram_dedup(None, FAKE, None, 1, 1000, FAKE, FAKE, FAKE, FAKE, need, None) == EINVAL
+
+
+def test_synth_fill_validation(hg):
+    L = hg.lib()
+    assert L.engram_synth_fill(FAKE, FAKE, 0, 0, 1, None) == ERANGE
+    assert L.engram_synth_fill(FAKE, FAKE, (1 << 32) + 1, 0, 1, None) == ERANGE
+    assert L.engram_synth_fill(FAKE, FAKE, 16, 48, 1, None) == EINVAL
+    assert L.engram_synth_fill(FAKE + 4, FAKE, 16, 0, 1, None) == EINVAL
+    assert L.engram_synth_fill(FAKE, FAKE + 2, 16, 0, 1, None) == EINVAL
+
+
+def test_status_strings(hg):
+    L = hg.lib()
+    for st in (OK, EINVAL, ERANGE, EWORKSPACE, EHIP, EUNSUPPORTED):
+        assert L.engram_status_string(st).decode().startswith(hg.STATUS[st])
+    assert b"unknown" in L.engram_status_string(-99)
+
+
+def test_binding_rejects_host_tensors(hg):
+    import torch
+    with pytest.raises(ValueError):
+        hg.Plan(torch.zeros((48, 4, 256), dtype=torch.uint8), torch.zeros((48, 4)))
+
+
+def test_no_cpu_fallback_in_package():
+    """The package's Python code never imports the oracle or the workloads generator."""
+    pkg = os.path.join(ROOT, "hashed_gram_memory_amd")
+    for f in glob.glob(os.path.join(pkg, "*.py")):
+        text = open(f).read()
+        assert "oracle" not in text.replace("oracle.", "") or "import oracle" not in text, f
+        assert "import oracle" not in text and "from oracle" not in text, f
+        assert "import workloads" not in text and "from workloads" not in text, f
