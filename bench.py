@@ -71,7 +71,7 @@ def cpu_baseline(ids, rows: int, seed: int, sample_tokens: int):
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"first {sample_tokens} tokens of the same 131072-token Zipf stream: oracle windows + hash + "
+        "sample": (f"first {sample_tokens} tokens of the 131072-token Zipf stream: oracle windows + hash + "
                    f"gather-reduce (numpy, float64) against full-size 48 x 2^{rows.bit_length() - 1} host tables "
                    f"(only touched rows resident); {dt:.1f} s"),
     }
@@ -82,7 +82,9 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-sample", type=int, default=32768, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=131072, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--id-batches", type=int, default=1,
                     help="rotate among this many seeded id batches of the same shape (1: the workload's own ids)")
     args = ap.parse_args(argv)
@@ -139,6 +141,13 @@ def main(argv=None) -> int:
         e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     hash_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     gather_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))

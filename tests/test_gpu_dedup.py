@@ -1,0 +1,102 @@
+"""GPU parity of the dedup pass: groups bit-exact against the oracle, and
+dedup-mode memory vectors bitwise equal to direct mode."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_support import device_tables, dummy_plan, lib, small_device_tables, to_dev_ids
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _check_groups(groups, ids, hist):
+    n_tok = ids.size
+    want_perm, want_off, want_nu = oracle.dedup(oracle.windows(ids, hist))
+    nu = int(groups.n_unique.item())
+    assert nu == want_nu
+    assert np.array_equal(groups.perm.cpu().numpy(), want_perm)
+    assert np.array_equal(groups.offsets[:nu + 1].cpu().numpy(), want_off)
+    assert want_off[-1] == n_tok
+
+
+@pytest.mark.parametrize("n_seq,seq_len,hi,with_hist", [
+    (1, 1, 10, False), (1, 2, 1, False), (1, 5, 3, True), (2, 300, 4, False), (3, 1000, 100, True),
+    (8, 517, 1 << 31, False), (1, 5000, 2, False), (64, 1, 129280, True), (4, 4096, 1 << 24, True),
+])
+def test_dedup_groups_exact(n_seq, seq_len, hi, with_hist):
+    _say(f"dedup {n_seq}x{seq_len} ids<{hi} hist={with_hist}")
+    rng = np.random.default_rng(seq_len + n_seq)
+    ids = rng.integers(0, hi, size=(n_seq, seq_len), dtype=np.int64).astype(np.int32)
+    hist = rng.integers(0, hi, size=(n_seq, 3), dtype=np.int64).astype(np.int32) if with_hist else None
+    plan = dummy_plan(4096)
+    groups = lib().dedup(plan, *to_dev_ids(ids, hist))
+    torch.cuda.synchronize()
+    _check_groups(groups, ids, hist)
+
+
+def test_dedup_shared_prefix_batch():
+    """Sequences sharing a prefix collapse to one group per prefix position."""
+    _say("dedup shared prefix 16 x (256 + 256)")
+    rng = np.random.default_rng(5)
+    prefix = rng.integers(0, 129280, size=256).astype(np.int32)
+    ids = np.concatenate([np.tile(prefix, (16, 1)), rng.integers(0, 129280, size=(16, 256)).astype(np.int32)], 1)
+    plan = dummy_plan(4096)
+    groups = lib().dedup(plan, *to_dev_ids(ids, None))
+    torch.cuda.synchronize()
+    _check_groups(groups, ids, None)
+    assert int(groups.n_unique.item()) <= 256 + 16 * 256
+
+
+def test_dedup_empty():
+    _say("dedup empty")
+    plan = dummy_plan(4096)
+    ids = torch.zeros((0, 5), dtype=torch.int32, device="cuda")
+    groups = lib().dedup(plan, ids, None)
+    torch.cuda.synchronize()
+    assert int(groups.n_unique.item()) == 0 and int(groups.offsets[0].item()) == 0
+
+
+def test_dedup_mode_equals_direct_small():
+    _say("dedup-mode gather == direct (small)")
+    R = 1024
+    host_t, host_c = workloads.dense_tables(77, R)
+    t, c = small_device_tables(host_t, host_c)
+    plan = lib().Plan(t, c)
+    rng = np.random.default_rng(2)
+    ids = rng.integers(0, 6, size=(7, 333)).astype(np.int32)  # many repeated windows
+    d_ids, _ = to_dev_ids(ids, None)
+    addr = lib().hash(plan, d_ids)
+    direct = lib().gather_reduce(plan, addr)
+    groups = lib().dedup(plan, d_ids)
+    dd = torch.full_like(direct, float("nan"))
+    lib().gather_reduce(plan, addr, out=dd, groups=groups)
+    torch.cuda.synchronize()
+    _check_groups(groups, ids, None)
+    assert torch.equal(dd, direct)
+
+
+def test_dedup_batched_shared_prefix_full_size():
+    """The batched shared-prefix workload at full size: exact groups, dedup == direct bitwise."""
+    w = workloads.WORKLOADS[5]
+    _say(f"dedup workload 5 full size n_tok={w.n_tok}")
+    ids, hist = workloads.make_ids(w)
+    t, c = device_tables(w.rows, w.table_seed)
+    plan = lib().Plan(t, c)
+    d_ids, d_hist = to_dev_ids(ids, hist)
+    addr = lib().hash(plan, d_ids, d_hist)
+    direct = lib().gather_reduce(plan, addr)
+    groups = lib().dedup(plan, d_ids, d_hist)
+    dd = torch.full_like(direct, float("nan"))
+    lib().gather_reduce(plan, addr, out=dd, groups=groups)
+    torch.cuda.synchronize()
+    _check_groups(groups, ids, hist)
+    nu = int(groups.n_unique.item())
+    _say(f"n_unique={nu} of {w.n_tok}")
+    assert nu < w.n_tok * 0.6
+    assert torch.equal(dd, direct)
