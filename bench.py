@@ -29,6 +29,17 @@ BYTES_PER_TOKEN = {  # algorithmic bytes of engram_gather_reduce per token
     "rows": 48 * 256, "scales": 48 * 4, "addresses": 48 * 4, "output": 2 * 256 * 4}
 GATHER_BYTES_PER_TOKEN = sum(BYTES_PER_TOKEN.values())  # 14,720
 HASH_BYTES_PER_TOKEN = 4 + 48 * 4  # id in, addresses out
+WORKLOAD_TEXT = {
+    1: "tiny: 1 x 512 uniform ids in [0, 1024); 48 sub-tables x 4096 rows x 256 B FP8 E4M3 + fp32 row scales",
+    2: ("decode: 64 sequences x 1 new token against a 3-token history, Zipf(1.1) ids over 129280; 48 sub-tables x "
+        "2^20 rows x 256 B FP8 E4M3 (12 GiB) + fp32 row scales"),
+    3: ("prefill: 1 x 32768 Zipf(1.1) ids over 129280; 48 sub-tables x 2^22 rows x 256 B FP8 E4M3 (48 GiB) + fp32 "
+        "row scales"),
+    4: ("full-size prefill: 1 x 131072 Zipf(1.1) ids over 129280; 48 sub-tables x 2^24 rows x 256 B FP8 E4M3 "
+        "(192 GiB) + fp32 row scales, resident in HBM"),
+    5: ("batched prefill with shared prefixes: 64 x (4096 shared + 4096 own) Zipf(1.1) ids over 129280; 48 "
+        "sub-tables x 2^24 rows x 256 B FP8 E4M3 (192 GiB) + fp32 row scales"),
+}
 PMC_FILE = os.path.join(ROOT, "profiles", "gather_reduce_full_131072_pmc.json")
 GATHER_SRC = os.path.join(ROOT, "hashed_gram_memory_amd", "csrc", "gather_reduce.hip")
 
@@ -85,6 +96,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-sample", type=int, default=131072, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="synthetic workload (4: the full-size prefill the metric is quoted on)")
+    ap.add_argument("--dedup", action="store_true", help="batched workloads: engram_dedup + dedup-mode gather")
     ap.add_argument("--id-batches", type=int, default=1,
                     help="rotate among this many seeded id batches of the same shape (1: the workload's own ids)")
     args = ap.parse_args(argv)
@@ -99,7 +113,7 @@ def main(argv=None) -> int:
     import hashed_gram_memory_amd as hg
     import workloads
 
-    w = workloads.WORKLOADS[4]
+    w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     n_tok = w.n_tok
@@ -109,19 +123,34 @@ def main(argv=None) -> int:
     scales = torch.empty((48, w.rows), dtype=torch.float32, device=dev)
     hg.synth_fill(tables, scales, w.table_seed)
     torch.cuda.synchronize()
-    plan = hg.Plan(tables, scales)
+    plan = hg.Plan(tables, scales, vocab_size=workloads.VOCAB if w.ids_kind != "uniform1024" else 1024)
 
     batches = []
     for b in range(args.id_batches):
-        ids, _ = workloads.make_ids(w, None if b == 0 else w.token_seed + 100 * b)
-        batches.append((ids, torch.from_numpy(ids).to(dev)))
+        ids, hist = workloads.make_ids(w, None if b == 0 else w.token_seed + 100 * b)
+        batches.append((ids, torch.from_numpy(ids).to(dev), None if hist is None else torch.from_numpy(hist).to(dev)))
     addr = torch.empty((n_tok, 48), dtype=torch.uint32, device=dev)
     out = torch.empty((n_tok, 2, 256), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    groups = ws = None
+    if args.dedup:
+        groups = hg.Groups(torch.empty(n_tok, dtype=torch.int32, device=dev),
+                           torch.empty(n_tok + 1, dtype=torch.int32, device=dev),
+                           torch.empty(1, dtype=torch.int32, device=dev))
+        ws = torch.empty(hg.dedup_workspace_bytes(n_tok), dtype=torch.uint8, device=dev)
+
+    def hash_phase(i):
+        b = batches[i % len(batches)]
+        hg.hash(plan, b[1], b[2], out=addr, stream=stream)
+        if args.dedup:
+            hg.dedup(plan, b[1], b[2], workspace=ws, groups=groups, stream=stream)
+
+    def gather_phase():
+        hg.gather_reduce(plan, addr, out=out, groups=groups, stream=stream)
 
     def step(i):
-        hg.hash(plan, batches[i % len(batches)][1], None, out=addr, stream=stream)
-        hg.gather_reduce(plan, addr, out=out, stream=stream)
+        hash_phase(i)
+        gather_phase()
 
     _log(f"warmup {args.warmup}")
     for i in range(args.warmup):
@@ -135,9 +164,9 @@ def main(argv=None) -> int:
     for i in range(args.steps):
         e = ev[i]
         e[0].record(stream)
-        hg.hash(plan, batches[i % len(batches)][1], None, out=addr, stream=stream)
+        hash_phase(i)
         e[1].record(stream)
-        hg.gather_reduce(plan, addr, out=out, stream=stream)
+        gather_phase()
         e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -153,11 +182,18 @@ def main(argv=None) -> int:
     gather_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_per_step = wall / args.steps * 1e3
     tok_s = n_tok / (ms_per_step / 1e3)
-    achieved = GATHER_BYTES_PER_TOKEN * n_tok / (gather_ms / 1e3) / 1e9
-    traffic = _traffic(n_tok)
+    n_unique = int(groups.n_unique.item()) if args.dedup else None
+    if args.dedup:
+        # one lookup per group (rows, scales, addresses, its offsets pair) + one perm read and one
+        # 2 KiB output store per token
+        gather_bytes = n_unique * (48 * 256 + 48 * 4 + 48 * 4 + 8) + n_tok * (4 + 2 * 256 * 4)
+    else:
+        gather_bytes = GATHER_BYTES_PER_TOKEN * n_tok
+    achieved = gather_bytes / (gather_ms / 1e3) / 1e9
+    traffic = _traffic(n_tok) if args.workload == 4 and not args.dedup and args.id_batches == 1 else None
 
     base = None
-    if args.cpu_sample > 0:
+    if args.cpu_sample > 0 and args.workload == 4:
         _log(f"cpu baseline: oracle on {args.cpu_sample} tokens")
         base = cpu_baseline(batches[0][0], w.rows, w.table_seed, min(args.cpu_sample, n_tok))
 
@@ -175,12 +211,13 @@ def main(argv=None) -> int:
         "dtype": "fp32",
         "data": "synthetic",
         "config": {
-            "workload": ("full-size prefill: 1 x 131072 Zipf(1.1) ids over 129280; 48 sub-tables x 2^24 rows x 256 B "
-                         "FP8 E4M3 (192 GiB) + fp32 row scales, resident in HBM"),
+            "workload": (WORKLOAD_TEXT[args.workload]),
             "n_tok": n_tok,
             "rows_per_subtable": w.rows,
             "id_batches": args.id_batches,
-            "step": "engram_hash + engram_gather_reduce",
+            "step": "engram_hash + engram_dedup + engram_gather_reduce (dedup mode)" if args.dedup
+                    else "engram_hash + engram_gather_reduce",
+            "n_unique": n_unique,
         },
         "roofline": {
             "bound": "hbm",
@@ -193,8 +230,9 @@ def main(argv=None) -> int:
         },
         "gather_ms": gather_ms,
         "hash_ms": hash_ms,
+        "us_per_step": ms_per_step * 1e3,
         "hash_gbps": HASH_BYTES_PER_TOKEN * n_tok / (hash_ms / 1e3) / 1e9,
-        "gather_bytes_per_token": GATHER_BYTES_PER_TOKEN,
+        "gather_bytes_per_launch": gather_bytes,
         "cpu_baseline": base,
     }
     print(json.dumps(rec), flush=True)

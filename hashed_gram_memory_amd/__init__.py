@@ -47,7 +47,7 @@ class PlanDesc(ctypes.Structure):
         ("max_order", ctypes.c_uint32),
         ("n_heads", ctypes.c_uint32),
         ("row_bytes", ctypes.c_uint32),
-        ("reserved0", ctypes.c_uint32),
+        ("vocab_size", ctypes.c_uint32),
         ("hash_seed", ctypes.c_uint64),
         ("rows", ctypes.POINTER(ctypes.c_uint64)),
         ("tables", ctypes.POINTER(ctypes.c_void_p)),
@@ -120,7 +120,7 @@ class Plan:
     The tensors are referenced (not copied) and kept alive by the plan.
     """
 
-    def __init__(self, tables, scales, hash_seed: int = DEFAULT_HASH_SEED):
+    def __init__(self, tables, scales, hash_seed: int = DEFAULT_HASH_SEED, vocab_size: int = 0):
         if isinstance(tables, torch.Tensor):
             if tables.dim() != 3 or tables.shape[0] != N_SUB or tables.shape[2] != ROW_BYTES:
                 raise ValueError("tables must be [48, R, 256]")
@@ -139,22 +139,24 @@ class Plan:
             _dev(t, torch.uint8, f"tables[{s}]")
             _dev(c, torch.float32, f"scales[{s}]")
             rows.append(t.shape[0])
-        self._build(rows, [t.data_ptr() for t in tables], [c.data_ptr() for c in scales], hash_seed,
+        self._build(rows, [t.data_ptr() for t in tables], [c.data_ptr() for c in scales], hash_seed, vocab_size,
                     keep=(tables, scales))
 
     @classmethod
-    def from_pointers(cls, rows, table_ptrs, scale_ptrs, hash_seed: int = DEFAULT_HASH_SEED, keep=None) -> "Plan":
+    def from_pointers(cls, rows, table_ptrs, scale_ptrs, hash_seed: int = DEFAULT_HASH_SEED, vocab_size: int = 0,
+                      keep=None) -> "Plan":
         """Plan over raw device pointers (48 each) with the given row counts; ``keep`` is held alive."""
         p = cls.__new__(cls)
-        p._build(list(rows), list(table_ptrs), list(scale_ptrs), hash_seed, keep)
+        p._build(list(rows), list(table_ptrs), list(scale_ptrs), hash_seed, vocab_size, keep)
         return p
 
-    def _build(self, rows, tab_ptrs, sc_ptrs, hash_seed, keep) -> None:
+    def _build(self, rows, tab_ptrs, sc_ptrs, hash_seed, vocab_size, keep) -> None:
         if len(rows) != N_SUB or len(tab_ptrs) != N_SUB or len(sc_ptrs) != N_SUB:
             raise ValueError("need 48 row counts, table pointers and scale pointers")
         self._handle = None
         self.rows = rows
         self.hash_seed = hash_seed
+        self.vocab_size = vocab_size
         self._keep = keep
         self._rows_c = (ctypes.c_uint64 * N_SUB)(*rows)
         self._tabs_c = (ctypes.c_void_p * N_SUB)(*tab_ptrs)
@@ -162,6 +164,7 @@ class Plan:
         desc = PlanDesc()
         _check(_lib.engram_plan_desc_init(ctypes.byref(desc)), "engram_plan_desc_init")
         desc.hash_seed = hash_seed
+        desc.vocab_size = vocab_size
         desc.rows = ctypes.cast(self._rows_c, ctypes.POINTER(ctypes.c_uint64))
         desc.tables = ctypes.cast(self._tabs_c, ctypes.POINTER(ctypes.c_void_p))
         desc.scales = ctypes.cast(self._scs_c, ctypes.POINTER(ctypes.c_void_p))

@@ -56,7 +56,7 @@ int engram_plan(const engram_plan_desc* d, engram_plan_t* out) {
         d->max_order != ENGRAM_MAX_ORDER || d->n_heads != ENGRAM_N_HEADS ||
         d->row_bytes != ENGRAM_ROW_BYTES)
         return ENGRAM_EUNSUPPORTED;
-    if (d->reserved0 != 0 || !d->rows || !d->tables || !d->scales) return ENGRAM_EINVAL;
+    if (!d->rows || !d->tables || !d->scales) return ENGRAM_EINVAL;
     for (int s = 0; s < kSub; ++s) {
         const uint64_t r = d->rows[s];
         if (r == 0 || r > (uint64_t(1) << 32)) return ENGRAM_ERANGE;
@@ -67,6 +67,7 @@ int engram_plan(const engram_plan_desc* d, engram_plan_t* out) {
     if (!p) return ENGRAM_EINVAL;
     memset(p, 0, sizeof(*p));
     p->hash_seed = d->hash_seed;
+    p->vocab_size = d->vocab_size;
     SplitMix64 g{d->hash_seed};
     for (int i = 0; i < kMult; ++i) p->hash.mult[i] = g.next() | 1u;
     for (int s = 0; s < kSub; ++s) {
@@ -140,8 +141,8 @@ int engram_dedup(engram_plan_t p, const int32_t* ids, const int32_t* history, in
     }
     const size_t need = dedup_workspace_bytes(uint32_t(n_tok));
     if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return ENGRAM_EWORKSPACE;
-    hipError_t e = launch_dedup(ids, history, uint32_t(n_tok), uint32_t(seq_len), perm, offsets, n_unique,
-                                ws, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_dedup(ids, history, uint32_t(n_tok), uint32_t(seq_len), p->vocab_size, perm, offsets,
+                                n_unique, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
 }
 

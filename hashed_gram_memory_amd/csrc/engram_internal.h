@@ -32,6 +32,7 @@ struct GatherParams {
 
 struct engram_plan_s {
     uint64_t hash_seed;
+    uint32_t vocab_size;
     engram::HashParams hash;
     engram::GatherParams gather;
 };
@@ -49,7 +50,10 @@ hipError_t launch_gather_reduce(const GatherParams& p, const uint32_t* addr, uin
 
 size_t dedup_workspace_bytes(uint32_t n_tok);
 
+uint32_t dedup_key_bits(uint32_t vocab_size);
+
 hipError_t launch_dedup(const int32_t* ids, const int32_t* history, uint32_t n_tok, uint32_t seq_len,
-                        int32_t* perm, int32_t* offsets, int32_t* n_unique, void* ws, hipStream_t stream);
+                        uint32_t vocab_size, int32_t* perm, int32_t* offsets, int32_t* n_unique, void* ws,
+                        hipStream_t stream);
 
 }  // namespace engram

@@ -8,12 +8,13 @@
 // (multiply-xor of the id window, then mod R_s) is this library's reading;
 // the pages do not print one.
 //
-// Layout: one thread per token.  The 192 multipliers and the 48 (R, magic)
-// pairs are kernel arguments indexed by compile-time constants, so they are
-// wave-uniform scalar loads; only the four window ids live in vector
-// registers.  Each thread writes its 48 addresses as 12 dwordx4 stores
-// (192 contiguous bytes per token).  The kernel is store-bound and tiny
-// next to the gather (196 B per token vs ~14.7 KB).
+// Layout: a block covers 64 tokens with 6 waves, one per (module, order);
+// lane l of every wave is token l of the block.  A wave's 8 heads share the
+// (module, order), so its 32 multipliers and its 8 (R, magic) pairs are
+// wave-uniform scalar loads from the kernel arguments; the thread reads its
+// token's window (4 ids, cached across the 6 waves) and writes its 8
+// addresses as two 16-byte stores (32 contiguous bytes).  The kernel is
+// store-bound and small next to the gather (196 B per token against ~14.7 KB).
 #include "engram_internal.h"
 
 namespace engram {
@@ -28,11 +29,14 @@ __device__ __forceinline__ uint32_t mod_rows(uint64_t x, uint64_t R, uint64_t ma
     return static_cast<uint32_t>(r);
 }
 
-__global__ __launch_bounds__(256) void hash_kernel(const HashParams P, const int32_t* __restrict__ ids,
+__global__ __launch_bounds__(384) void hash_kernel(const HashParams P, const int32_t* __restrict__ ids,
                                                    const int32_t* __restrict__ history, uint32_t n_tok,
                                                    uint32_t seq_len, uint32_t* __restrict__ addr) {
-    const uint32_t tok = blockIdx.x * 256u + threadIdx.x;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (module, order) = (wave/3, 2+wave%3)
+    const uint32_t tok = blockIdx.x * 64u + (threadIdx.x & 63u);
     if (tok >= n_tok) return;
+    const uint32_t m = wave / 3u;
+    const uint32_t order = ENGRAM_MIN_ORDER + wave % 3u;
     const uint32_t seq = tok / seq_len;
     const int32_t t = static_cast<int32_t>(tok - seq * seq_len);
 
@@ -49,34 +53,28 @@ __global__ __launch_bounds__(256) void hash_kernel(const HashParams P, const int
         w[k] = static_cast<uint32_t>(v);
     }
 
-    uint32_t a[kSub];
+    const uint32_t mbase = wave * (ENGRAM_N_HEADS * ENGRAM_MAX_ORDER);  // multipliers of (m, order, head 0, k 0)
+    const uint32_t s0 = m * kRowsPerModule + (order - ENGRAM_MIN_ORDER) * ENGRAM_N_HEADS;
+    uint32_t a[ENGRAM_N_HEADS];
 #pragma unroll
-    for (int m = 0; m < ENGRAM_N_MODULES; ++m) {
+    for (int h = 0; h < ENGRAM_N_HEADS; ++h) {
+        uint64_t x = 0;
 #pragma unroll
-        for (int n = ENGRAM_MIN_ORDER; n <= ENGRAM_MAX_ORDER; ++n) {
-#pragma unroll
-            for (int h = 0; h < ENGRAM_N_HEADS; ++h) {
-                const int base = ((m * 3 + (n - ENGRAM_MIN_ORDER)) * ENGRAM_N_HEADS + h) * ENGRAM_MAX_ORDER;
-                uint64_t x = 0;
-#pragma unroll
-                for (int k = 0; k < n; ++k) x ^= w[k] * P.mult[base + k];
-                const int s = m * kRowsPerModule + (n - ENGRAM_MIN_ORDER) * ENGRAM_N_HEADS + h;
-                a[s] = mod_rows(x, P.rows[s], P.magic[s]);
-            }
-        }
+        for (int k = 0; k < ENGRAM_MAX_ORDER; ++k)
+            if (static_cast<uint32_t>(k) < order) x ^= w[k] * P.mult[mbase + h * ENGRAM_MAX_ORDER + k];
+        a[h] = mod_rows(x, P.rows[s0 + h], P.magic[s0 + h]);
     }
-
-    uint4* dst = reinterpret_cast<uint4*>(addr + static_cast<size_t>(tok) * kSub);
-#pragma unroll
-    for (int i = 0; i < kSub / 4; ++i) dst[i] = make_uint4(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]);
+    uint4* dst = reinterpret_cast<uint4*>(addr + static_cast<size_t>(tok) * kSub + s0);
+    dst[0] = make_uint4(a[0], a[1], a[2], a[3]);
+    dst[1] = make_uint4(a[4], a[5], a[6], a[7]);
 }
 
 }  // namespace
 
 hipError_t launch_hash(const HashParams& p, const int32_t* ids, const int32_t* history, uint32_t n_tok,
                        uint32_t seq_len, uint32_t* addr, hipStream_t stream) {
-    const uint32_t blocks = (n_tok + 255u) / 256u;
-    hipLaunchKernelGGL(hash_kernel, dim3(blocks), dim3(256), 0, stream, p, ids, history, n_tok, seq_len, addr);
+    const uint32_t blocks = (n_tok + 63u) / 64u;
+    hipLaunchKernelGGL(hash_kernel, dim3(blocks), dim3(384), 0, stream, p, ids, history, n_tok, seq_len, addr);
     return hipGetLastError();
 }
 

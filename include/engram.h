@@ -75,6 +75,11 @@ typedef enum engram_status {
  *
  *   n_modules, min_order, max_order, n_heads, row_bytes
  *       Must equal 2, 2, 4, 8, 256 (else ENGRAM_EUNSUPPORTED).
+ *   vocab_size
+ *       Exclusive upper bound of the token ids (the vocabulary the ids are
+ *       drawn from), or 0 when ids may take any value in [0, 2^31).  Only
+ *       engram_dedup uses it: it packs a window into 4*ceil(log2(vocab_size))
+ *       bits, so an id >= vocab_size breaks its grouping (not checked).
  *   hash_seed
  *       Seeds the 192 hash multipliers: M[i] is output i+1 of splitmix64
  *       (Steele, Lea and Flood 2014) seeded with hash_seed, with bit 0 set;
@@ -96,7 +101,7 @@ typedef struct engram_plan_desc {
     uint32_t max_order;
     uint32_t n_heads;
     uint32_t row_bytes;
-    uint32_t reserved0;            /* must be 0 */
+    uint32_t vocab_size;           /* exclusive bound of token ids; 0 = any id in [0, 2^31) */
     uint64_t hash_seed;
     const uint64_t* rows;
     const uint8_t* const* tables;

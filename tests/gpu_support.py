@@ -54,11 +54,12 @@ def small_device_tables(host_tabs, host_scs):
     return t, c
 
 
-def dummy_plan(rows: int):
-    """A plan whose tables are never read (hash-only tests): every pointer is one small buffer."""
+def dummy_plan(rows: int, vocab_size: int = 0):
+    """A plan whose tables are never read (hash and dedup tests): every pointer is one small buffer."""
     t = torch.zeros((1, 256), dtype=torch.uint8, device="cuda")
     c = torch.zeros(1, dtype=torch.float32, device="cuda")
-    return lib().Plan.from_pointers([rows] * 48, [t.data_ptr()] * 48, [c.data_ptr()] * 48, keep=(t, c))
+    return lib().Plan.from_pointers([rows] * 48, [t.data_ptr()] * 48, [c.data_ptr()] * 48, vocab_size=vocab_size,
+                                    keep=(t, c))
 
 
 def to_dev_ids(ids, history):

@@ -80,9 +80,12 @@ def test_plan_validation(hg):
         d2, k2 = _desc(hg)
         setattr(d2, field, val)
         assert _plan(hg, d2)[0] == EUNSUPPORTED, field
-    d2, k2 = _desc(hg)
-    d2.reserved0 = 1
-    assert _plan(hg, d2)[0] == EINVAL
+    for vocab in (1, 129280, (1 << 31), (1 << 32) - 1):
+        d2, k2 = _desc(hg)
+        d2.vocab_size = vocab
+        st, h = _plan(hg, d2)
+        assert st == OK
+        L.engram_plan_destroy(h)
     for rows, want in (([0] * 48, ERANGE), ([(1 << 32) + 1] * 48, ERANGE), ([1 << 32] * 48, OK), ([1] * 48, OK)):
         d2, k2 = _desc(hg, rows=rows)
         st, h = _plan(hg, d2)

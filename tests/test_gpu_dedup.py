@@ -25,16 +25,17 @@ def _check_groups(groups, ids, hist):
     assert want_off[-1] == n_tok
 
 
-@pytest.mark.parametrize("n_seq,seq_len,hi,with_hist", [
-    (1, 1, 10, False), (1, 2, 1, False), (1, 5, 3, True), (2, 300, 4, False), (3, 1000, 100, True),
-    (8, 517, 1 << 31, False), (1, 5000, 2, False), (64, 1, 129280, True), (4, 4096, 1 << 24, True),
+@pytest.mark.parametrize("n_seq,seq_len,hi,with_hist,vocab", [
+    (1, 1, 10, False, 0), (1, 2, 1, False, 1), (1, 5, 3, True, 3), (2, 300, 4, False, 0), (3, 1000, 100, True, 100),
+    (8, 517, 1 << 31, False, 0), (1, 5000, 2, False, 2), (64, 1, 129280, True, 129280),
+    (4, 4096, 1 << 24, True, 1 << 24), (3, 3000, 129280, False, 129280), (2, 2500, 70000, True, 0),
 ])
-def test_dedup_groups_exact(n_seq, seq_len, hi, with_hist):
-    _say(f"dedup {n_seq}x{seq_len} ids<{hi} hist={with_hist}")
+def test_dedup_groups_exact(n_seq, seq_len, hi, with_hist, vocab):
+    _say(f"dedup {n_seq}x{seq_len} ids<{hi} hist={with_hist} vocab={vocab}")
     rng = np.random.default_rng(seq_len + n_seq)
     ids = rng.integers(0, hi, size=(n_seq, seq_len), dtype=np.int64).astype(np.int32)
     hist = rng.integers(0, hi, size=(n_seq, 3), dtype=np.int64).astype(np.int32) if with_hist else None
-    plan = dummy_plan(4096)
+    plan = dummy_plan(4096, vocab)
     groups = lib().dedup(plan, *to_dev_ids(ids, hist))
     torch.cuda.synchronize()
     _check_groups(groups, ids, hist)
@@ -46,7 +47,7 @@ def test_dedup_shared_prefix_batch():
     rng = np.random.default_rng(5)
     prefix = rng.integers(0, 129280, size=256).astype(np.int32)
     ids = np.concatenate([np.tile(prefix, (16, 1)), rng.integers(0, 129280, size=(16, 256)).astype(np.int32)], 1)
-    plan = dummy_plan(4096)
+    plan = dummy_plan(4096, 129280)
     groups = lib().dedup(plan, *to_dev_ids(ids, None))
     torch.cuda.synchronize()
     _check_groups(groups, ids, None)
@@ -67,7 +68,7 @@ def test_dedup_mode_equals_direct_small():
     R = 1024
     host_t, host_c = workloads.dense_tables(77, R)
     t, c = small_device_tables(host_t, host_c)
-    plan = lib().Plan(t, c)
+    plan = lib().Plan(t, c, vocab_size=6)
     rng = np.random.default_rng(2)
     ids = rng.integers(0, 6, size=(7, 333)).astype(np.int32)  # many repeated windows
     d_ids, _ = to_dev_ids(ids, None)
@@ -87,7 +88,7 @@ def test_dedup_batched_shared_prefix_full_size():
     _say(f"dedup workload 5 full size n_tok={w.n_tok}")
     ids, hist = workloads.make_ids(w)
     t, c = device_tables(w.rows, w.table_seed)
-    plan = lib().Plan(t, c)
+    plan = lib().Plan(t, c, vocab_size=workloads.VOCAB)
     d_ids, d_hist = to_dev_ids(ids, hist)
     addr = lib().hash(plan, d_ids, d_hist)
     direct = lib().gather_reduce(plan, addr)
