@@ -88,6 +88,40 @@ def cpu_baseline(ids, rows: int, seed: int, sample_tokens: int):
     }
 
 
+def _median_ms(torch, fn, stream, reps: int) -> float:
+    fn()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return float(np.median(times))
+
+
+def measure_ceiling(hg, torch, plan, tables, addr, out, stream):
+    """What the memory system delivers on this device: streaming read and copy, and the gather without scales."""
+    flat = tables.view(-1)
+    read_bytes = min(8 << 30, flat.numel())
+    sink = torch.zeros(1, dtype=torch.int32, device=tables.device)
+    t_read = _median_ms(torch, lambda: hg.probe_read(flat[:read_bytes], sink, stream=stream), stream, 5)
+    copy_bytes = 2 << 30
+    dst = torch.empty(copy_bytes, dtype=torch.uint8, device=tables.device)
+    t_copy = _median_ms(torch, lambda: hg.probe_copy(flat[:copy_bytes], dst, stream=stream), stream, 5)
+    del dst
+    n_tok = addr.shape[0]
+    t_rows = _median_ms(torch, lambda: hg.probe_rows(plan, addr, out, stream=stream), stream, 10)
+    rows_bytes = n_tok * (48 * 256 + 48 * 4 + 2 * 256 * 4)
+    return {
+        "stream_read_GBps": read_bytes / (t_read / 1e3) / 1e9,
+        "stream_copy_GBps": 2 * copy_bytes / (t_copy / 1e3) / 1e9,
+        "gather_rows_only_us": t_rows * 1e3,
+        "gather_rows_only_GBps": rows_bytes / (t_rows / 1e3) / 1e9,
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +133,7 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
                     help="synthetic workload (4: the full-size prefill the metric is quoted on)")
     ap.add_argument("--dedup", action="store_true", help="batched workloads: engram_dedup + dedup-mode gather")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the memory-ceiling probes")
     ap.add_argument("--id-batches", type=int, default=1,
                     help="rotate among this many seeded id batches of the same shape (1: the workload's own ids)")
     args = ap.parse_args(argv)
@@ -178,6 +213,8 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    ceiling = None if args.no_ceiling or args.dedup else measure_ceiling(hg, torch, plan, tables, addr, out, stream)
+
     hash_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     gather_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_per_step = wall / args.steps * 1e3
@@ -233,8 +270,11 @@ def main(argv=None) -> int:
         "us_per_step": ms_per_step * 1e3,
         "hash_gbps": HASH_BYTES_PER_TOKEN * n_tok / (hash_ms / 1e3) / 1e9,
         "gather_bytes_per_launch": gather_bytes,
+        "ceiling": ceiling,
         "cpu_baseline": base,
     }
+    if ceiling:
+        rec["ceiling"]["gather_vs_read_ceiling"] = achieved / ceiling["stream_read_GBps"]
     print(json.dumps(rec), flush=True)
     return 0
 

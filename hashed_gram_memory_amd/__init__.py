@@ -70,6 +70,9 @@ def _load():
         "engram_dedup_workspace": [I64, ctypes.POINTER(ctypes.c_size_t)],
         "engram_dedup": [P, VP, VP, I64, I64, VP, VP, VP, VP, ctypes.c_size_t, VP],
         "engram_synth_fill": [VP, VP, U64, U32, U64, VP],
+        "engram_probe_read": [VP, U64, VP, VP],
+        "engram_probe_copy": [VP, VP, U64, VP],
+        "engram_probe_rows": [P, VP, I64, VP, VP],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -295,3 +298,34 @@ def synth_fill(tables, scales, seed: int, stream=None) -> None:
         st = _lib.engram_synth_fill(_dev(t, torch.uint8, "table"), _dev(c, torch.float32, "scales"), t.shape[0], s,
                                     seed, _stream(stream))
         _check(st, "engram_synth_fill")
+
+
+# ---------------------------------------------------------------------------
+# Memory-ceiling probes (measurement only; include/engram_probe.h)
+# ---------------------------------------------------------------------------
+
+def probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Stream-read every byte of the contiguous device tensor ``src``."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    _check(_lib.engram_probe_read(src.data_ptr(), nbytes - nbytes % 16, _dev(sink, torch.int32, "sink"),
+                                  _stream(stream)), "engram_probe_read")
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Stream-copy ``src`` into ``dst`` (same byte size, contiguous, device)."""
+    nbytes = src.numel() * src.element_size()
+    if nbytes != dst.numel() * dst.element_size() or not (src.is_cuda and dst.is_cuda):
+        raise ValueError("src and dst must be device tensors of the same byte size")
+    _check(_lib.engram_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes - nbytes % 16, _stream(stream)),
+           "engram_probe_copy")
+
+
+def probe_rows(plan: Plan, addr: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """The gather without its scale reads (engram_probe_rows)."""
+    if addr.dim() != 2 or addr.shape[1] != N_SUB or tuple(out.shape) != (addr.shape[0], N_MODULES, ROW_BYTES):
+        raise ValueError("addr must be [n_tok, 48] and out [n_tok, 2, 256]")
+    _check(_lib.engram_probe_rows(plan.handle, _dev(addr, torch.uint32, "addr"), addr.shape[0],
+                                  _dev(out, torch.float32, "out"), _stream(stream)), "engram_probe_rows")
+    return out

@@ -1,0 +1,46 @@
+/*
+ * engram_probe.h -- memory-ceiling probes (measurement only; not part of the
+ * lookup).
+ *
+ * The lookup's gather is bound by HBM.  These kernels measure, on the same
+ * device and in the same process, what the memory system delivers for the
+ * access patterns involved, so the gather's achieved bandwidth can be read
+ * against a measured ceiling as well as against the 8 TB/s datasheet peak:
+ *   - a streaming read and a streaming copy (16-byte vector accesses);
+ *   - the gather itself with the row scales left out (rows only): the same
+ *     wave layout and row loads as engram_gather_reduce, decoded rows summed
+ *     without scaling, so its cost minus the full kernel's is the cost of the
+ *     48 random 4-byte scale reads.
+ * All return 0 or a negative engram_status; all are asynchronous on
+ * `stream` and allocate nothing.
+ */
+#ifndef ENGRAM_PROBE_H
+#define ENGRAM_PROBE_H
+
+#include <stdint.h>
+
+#include "engram.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` (a multiple of 16) from device memory `src` (16-byte
+ * aligned); `sink` is a device uint32 written only in a case that never
+ * occurs in practice, to keep the reads alive. */
+int engram_probe_read(const void* src, uint64_t bytes, uint32_t* sink, void* stream);
+
+/* Copy `bytes` (a multiple of 16) from `src` to `dst` (both 16-byte aligned,
+ * not overlapping). */
+int engram_probe_copy(const void* src, void* dst, uint64_t bytes, void* stream);
+
+/* engram_gather_reduce in direct mode without the row scales: out[tok][m][j]
+ * = sum over the module's 24 rows of the decoded code.  Same arguments and
+ * checks as engram_gather_reduce. */
+int engram_probe_rows(engram_plan_t plan, const uint32_t* addr, int64_t n_tok, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_PROBE_H */

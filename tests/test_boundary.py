@@ -205,3 +205,18 @@ def test_no_cpu_fallback_in_package():
         assert "oracle" not in text.replace("oracle.", "") or "import oracle" not in text, f
         assert "import oracle" not in text and "from oracle" not in text, f
         assert "import workloads" not in text and "from workloads" not in text, f
+
+
+def test_probe_validation(hg, plan):
+    L = hg.lib()
+    assert L.engram_probe_read(None, 16, FAKE, None) == EINVAL
+    assert L.engram_probe_read(FAKE, 17, FAKE, None) == EINVAL
+    assert L.engram_probe_read(FAKE + 8, 16, FAKE, None) == EINVAL
+    assert L.engram_probe_read(FAKE, 0, FAKE, None) == OK
+    assert L.engram_probe_copy(FAKE, FAKE + 256, 1024, None) == EINVAL  # overlap
+    assert L.engram_probe_copy(FAKE, None, 1024, None) == EINVAL
+    assert L.engram_probe_copy(FAKE, FAKE + 4096, 0, None) == OK
+    assert L.engram_probe_rows(None, FAKE, 1, FAKE, None) == EINVAL
+    assert L.engram_probe_rows(plan, FAKE, -1, FAKE, None) == ERANGE
+    assert L.engram_probe_rows(plan, FAKE, 0, FAKE, None) == OK
+    assert L.engram_probe_rows(plan, FAKE, 1, FAKE + 4, None) == EINVAL

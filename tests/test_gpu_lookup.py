@@ -242,3 +242,23 @@ def test_error_paths_leave_output_untouched():
     assert st == -1  # partial dedup pointer set
     torch.cuda.synchronize()
     assert torch.all(buf == 3.0)
+
+
+def test_probe_rows_equals_gather_with_unit_scales():
+    _say("probe rows == gather with unit scales")
+    R = 256
+    host_t, _ = workloads.dense_tables(31, R)
+    host_c = [np.ones(R, np.float32) for _ in range(48)]
+    t, c = small_device_tables(host_t, host_c)
+    plan = lib().Plan(t, c)
+    rng = np.random.default_rng(4)
+    addr = torch.from_numpy(rng.integers(0, R, size=(333, 48)).astype(np.int32)).cuda().view(torch.uint32)
+    a = lib().gather_reduce(plan, addr)
+    b = lib().probe_rows(plan, addr, torch.empty_like(a))
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lib().probe_read(t[0], sink)
+    dst = torch.empty_like(t[1])
+    lib().probe_copy(t[1], dst)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(dst, t[1])
