@@ -214,6 +214,13 @@ def main(argv=None) -> int:
         del src, dst
 
     ceiling = None if args.no_ceiling or args.dedup else measure_ceiling(hg, torch, plan, tables, addr, out, stream)
+    fused = None
+    if not args.dedup:
+        # the same step as one fused launch (engram_lookup): addresses never leave the wave
+        b0 = batches[0]
+        t_fused = _median_ms(torch, lambda: hg.lookup(plan, b0[1], b0[2], out=out, stream=stream), stream,
+                             max(5, min(args.steps, 50)))
+        fused = {"us_per_step": t_fused * 1e3, "tokens_per_s": n_tok / (t_fused / 1e3)}
 
     hash_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     gather_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
@@ -270,6 +277,7 @@ def main(argv=None) -> int:
         "us_per_step": ms_per_step * 1e3,
         "hash_gbps": HASH_BYTES_PER_TOKEN * n_tok / (hash_ms / 1e3) / 1e9,
         "gather_bytes_per_launch": gather_bytes,
+        "fused_lookup": fused,
         "ceiling": ceiling,
         "cpu_baseline": base,
     }

@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the lookup runs in the library's
 HIP kernels.  PyTorch provides device memory and streams.  The library must
-be built (``python -m hashed_gram_memory_amd.build``); importing this package
+be built (``python hashed_gram_memory_amd/build.py``); importing this package
 without it raises ImportError -- there is no fallback path.
 
 Functions mirror the C ABI in include/engram.h:
@@ -57,7 +57,7 @@ class PlanDesc(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m hashed_gram_memory_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python hashed_gram_memory_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, U64, U32, VP = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p
     sig = {
@@ -67,6 +67,7 @@ def _load():
         "engram_plan_multipliers": [P, ctypes.POINTER(ctypes.c_uint64)],
         "engram_hash": [P, VP, VP, I64, I64, VP, VP],
         "engram_gather_reduce": [P, VP, I64, VP, VP, VP, VP, VP],
+        "engram_lookup": [P, VP, VP, I64, I64, VP, VP],
         "engram_dedup_workspace": [I64, ctypes.POINTER(ctypes.c_size_t)],
         "engram_dedup": [P, VP, VP, I64, I64, VP, VP, VP, VP, ctypes.c_size_t, VP],
         "engram_synth_fill": [VP, VP, U64, U32, U64, VP],
@@ -250,6 +251,22 @@ def gather_reduce(plan: Plan, addr: torch.Tensor, out: torch.Tensor | None = Non
     st = _lib.engram_gather_reduce(plan.handle, _dev(addr, torch.uint32, "addr"), n_tok, perm, offsets, n_unique,
                                    _dev(out, torch.float32, "out"), _stream(stream))
     _check(st, "engram_gather_reduce")
+    return out
+
+
+def lookup(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, out: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """Hash and gather-reduce in one launch: fp32 [n_seq*seq_len, 2, 256] (engram_lookup)."""
+    n_seq, seq_len = _ids_shape(ids, history)
+    n_tok = n_seq * seq_len
+    if out is None:
+        out = torch.empty((n_tok, N_MODULES, ROW_BYTES), dtype=torch.float32, device=ids.device)
+    elif tuple(out.shape) != (n_tok, N_MODULES, ROW_BYTES):
+        raise ValueError("out must be [n_tok, 2, 256]")
+    st = _lib.engram_lookup(plan.handle, _dev(ids, torch.int32, "ids"),
+                            None if history is None else _dev(history, torch.int32, "history"), n_seq, seq_len,
+                            _dev(out, torch.float32, "out"), _stream(stream))
+    _check(st, "engram_lookup")
     return out
 
 

@@ -1,6 +1,6 @@
 """Build libengram.so (HIP kernels + C ABI) for gfx950 with hipcc.
 
-Usage: python -m hashed_gram_memory_amd.build
+Usage: python hashed_gram_memory_amd/build.py   (run by path: importing the package needs the library)
 Cross-compiles without a GPU.  Object files go to _build/ next to this file.
 """
 from __future__ import annotations
@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libengram.so")
-SOURCES = ["engram_api.cpp", "hash.hip", "gather_reduce.hip", "dedup.hip", "synth_fill.hip", "probe.hip"]
+SOURCES = ["engram_api.cpp", "hash.hip", "gather_reduce.hip", "dedup.hip", "synth_fill.hip", "probe.hip", "lookup.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.

@@ -120,6 +120,20 @@ int engram_gather_reduce(engram_plan_t p, const uint32_t* addr, int64_t n_tok, c
     return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
 }
 
+int engram_lookup(engram_plan_t p, const int32_t* ids, const int32_t* history, int64_t n_seq, int64_t seq_len,
+                  float* out, void* stream) {
+    if (!valid_plan(p)) return ENGRAM_EINVAL;
+    int64_t n_tok = 0;
+    int st = check_tokens(n_seq, seq_len, &n_tok);
+    if (st != ENGRAM_OK) return st;
+    if (n_tok == 0) return ENGRAM_OK;
+    if (!ids || !out || !aligned(ids, 4) || !aligned(out, 16)) return ENGRAM_EINVAL;
+    if (history && !aligned(history, 4)) return ENGRAM_EINVAL;
+    hipError_t e = launch_lookup(p->hash, p->gather, ids, history, uint32_t(n_tok), uint32_t(seq_len), out,
+                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
+}
+
 int engram_dedup_workspace(int64_t n_tok, size_t* bytes) {
     if (!bytes) return ENGRAM_EINVAL;
     if (n_tok < 0 || n_tok > kMaxTokens) return ENGRAM_ERANGE;

@@ -48,6 +48,9 @@ hipError_t launch_gather_reduce(const GatherParams& p, const uint32_t* addr, uin
                                 const int32_t* perm, const int32_t* offsets, const int32_t* n_unique,
                                 float* out, hipStream_t stream);
 
+hipError_t launch_lookup(const HashParams& h, const GatherParams& g, const int32_t* ids, const int32_t* history,
+                         uint32_t n_tok, uint32_t seq_len, float* out, hipStream_t stream);
+
 size_t dedup_workspace_bytes(uint32_t n_tok);
 
 uint32_t dedup_key_bits(uint32_t vocab_size);

@@ -29,6 +29,25 @@ __device__ __forceinline__ uint32_t mod_rows(uint64_t x, uint64_t R, uint64_t ma
     return static_cast<uint32_t>(r);
 }
 
+// The 8 addresses of one (module, order) for a window; ORDER and the
+// power-of-two case are compile-time so the loops and the modulus are
+// straight-line code.
+template <int ORDER, bool POW2>
+__device__ __forceinline__ void hash_heads(const HashParams& P, const uint64_t (&w)[ENGRAM_MAX_ORDER], uint32_t mbase,
+                                           uint32_t s0, uint32_t (&a)[ENGRAM_N_HEADS]) {
+#pragma unroll
+    for (int h = 0; h < ENGRAM_N_HEADS; ++h) {
+        uint64_t x = 0;
+#pragma unroll
+        for (int k = 0; k < ORDER; ++k) x ^= w[k] * P.mult[mbase + h * ENGRAM_MAX_ORDER + k];
+        if (POW2)
+            a[h] = static_cast<uint32_t>(x & (P.rows[s0 + h] - 1u));  // R = 2^k: x mod R is the low k bits
+        else
+            a[h] = mod_rows(x, P.rows[s0 + h], P.magic[s0 + h]);
+    }
+}
+
+template <bool POW2>
 __global__ __launch_bounds__(384) void hash_kernel(const HashParams P, const int32_t* __restrict__ ids,
                                                    const int32_t* __restrict__ history, uint32_t n_tok,
                                                    uint32_t seq_len, uint32_t* __restrict__ addr) {
@@ -36,7 +55,7 @@ __global__ __launch_bounds__(384) void hash_kernel(const HashParams P, const int
     const uint32_t tok = blockIdx.x * 64u + (threadIdx.x & 63u);
     if (tok >= n_tok) return;
     const uint32_t m = wave / 3u;
-    const uint32_t order = ENGRAM_MIN_ORDER + wave % 3u;
+    const uint32_t oi = wave % 3u;  // order - 2
     const uint32_t seq = tok / seq_len;
     const int32_t t = static_cast<int32_t>(tok - seq * seq_len);
 
@@ -54,16 +73,14 @@ __global__ __launch_bounds__(384) void hash_kernel(const HashParams P, const int
     }
 
     const uint32_t mbase = wave * (ENGRAM_N_HEADS * ENGRAM_MAX_ORDER);  // multipliers of (m, order, head 0, k 0)
-    const uint32_t s0 = m * kRowsPerModule + (order - ENGRAM_MIN_ORDER) * ENGRAM_N_HEADS;
+    const uint32_t s0 = m * kRowsPerModule + oi * ENGRAM_N_HEADS;
     uint32_t a[ENGRAM_N_HEADS];
-#pragma unroll
-    for (int h = 0; h < ENGRAM_N_HEADS; ++h) {
-        uint64_t x = 0;
-#pragma unroll
-        for (int k = 0; k < ENGRAM_MAX_ORDER; ++k)
-            if (static_cast<uint32_t>(k) < order) x ^= w[k] * P.mult[mbase + h * ENGRAM_MAX_ORDER + k];
-        a[h] = mod_rows(x, P.rows[s0 + h], P.magic[s0 + h]);
-    }
+    if (oi == 0)
+        hash_heads<2, POW2>(P, w, mbase, s0, a);
+    else if (oi == 1)
+        hash_heads<3, POW2>(P, w, mbase, s0, a);
+    else
+        hash_heads<4, POW2>(P, w, mbase, s0, a);
     uint4* dst = reinterpret_cast<uint4*>(addr + static_cast<size_t>(tok) * kSub + s0);
     dst[0] = make_uint4(a[0], a[1], a[2], a[3]);
     dst[1] = make_uint4(a[4], a[5], a[6], a[7]);
@@ -74,7 +91,13 @@ __global__ __launch_bounds__(384) void hash_kernel(const HashParams P, const int
 hipError_t launch_hash(const HashParams& p, const int32_t* ids, const int32_t* history, uint32_t n_tok,
                        uint32_t seq_len, uint32_t* addr, hipStream_t stream) {
     const uint32_t blocks = (n_tok + 63u) / 64u;
-    hipLaunchKernelGGL(hash_kernel, dim3(blocks), dim3(384), 0, stream, p, ids, history, n_tok, seq_len, addr);
+    bool pow2 = true;
+    for (int s = 0; s < kSub; ++s) pow2 = pow2 && (p.rows[s] & (p.rows[s] - 1u)) == 0;
+    if (pow2)
+        hipLaunchKernelGGL(hash_kernel<true>, dim3(blocks), dim3(384), 0, stream, p, ids, history, n_tok, seq_len, addr);
+    else
+        hipLaunchKernelGGL(hash_kernel<false>, dim3(blocks), dim3(384), 0, stream, p, ids, history, n_tok, seq_len,
+                           addr);
     return hipGetLastError();
 }
 

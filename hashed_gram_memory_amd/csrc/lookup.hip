@@ -1,0 +1,130 @@
+// Fused lookup: hash and gather-reduce in one kernel, no address buffer.
+//
+// The row addresses depend on the token ids alone [DeepSeek V4.1 Flash: The
+// VRAM Killer, section "What makes up the 511 GB of weights?"; How to Run
+// DeepSeek-V4.1-Flash: 510 GB, and 203 GB of It Is a Lookup Table, section
+// "Engram: the table that is never multiplied"], so the wave that gathers a
+// (token, module) can compute its own 24 addresses instead of reading them.
+// This drops the 192-byte address write and read per token and one launch,
+// which is what a decode step of a few tokens is made of.
+//
+// Mapping: as gather_reduce_kernel (one wave per (token, module), XCDs 0-3
+// module 0, XCDs 4-7 module 1).  The window ids, the multipliers and the 24
+// addresses are wave-uniform (scalar registers); the hash is the same
+// multiply-xor and modulus as hash_kernel, and the accumulation the same
+// fused multiply-add sequence as gather_reduce_kernel, so the result is
+// bitwise identical to engram_hash followed by engram_gather_reduce.
+#include "engram_internal.h"
+
+namespace engram {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct LookupParams {
+    HashParams h;
+    GatherParams g;
+};
+
+__device__ __forceinline__ uint32_t mod_rows(uint64_t x, uint64_t R, uint64_t magic) {
+    const uint64_t q = __umul64hi(x, magic);
+    uint64_t r = x - q * R;
+    if (r >= R) r -= R;
+    return static_cast<uint32_t>(r);
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const int32_t* __restrict__ ids,
+                                                     const int32_t* __restrict__ history, uint32_t tok_base,
+                                                     uint32_t n_tok, uint32_t seq_len, float* __restrict__ out) {
+    const uint32_t b = blockIdx.x;
+    const uint32_t xcd = b & 7u;
+    const uint32_t m = xcd >> 2;
+    const uint32_t group = (b >> 3) * 4u + (xcd & 3u);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t tok = tok_base + group * 4u + wave;
+    if (tok >= n_tok) return;
+
+    // Window of the token (wave-uniform): w[k] = id k positions back, else history, else 0.
+    const uint32_t seq = tok / seq_len;
+    const int32_t t = static_cast<int32_t>(tok - seq * seq_len);
+    uint64_t w[ENGRAM_MAX_ORDER];
+#pragma unroll
+    for (int k = 0; k < ENGRAM_MAX_ORDER; ++k) {
+        int32_t v = 0;
+        if (t - k >= 0)
+            v = ids[tok - k];
+        else if (history)
+            v = history[seq * 3u + static_cast<uint32_t>(3 + t - k)];
+        w[k] = static_cast<uint32_t>(v);
+    }
+
+    // The module's 24 addresses: q = 8*(order-2) + head.
+    const uint32_t s0 = m * kRowsPerModule;
+    const uint32_t mb = m * (kRowsPerModule * ENGRAM_MAX_ORDER);
+    uint32_t a[kRowsPerModule];
+#pragma unroll
+    for (int q = 0; q < kRowsPerModule; ++q) {
+        constexpr int kHeads = ENGRAM_N_HEADS;
+        const int order = ENGRAM_MIN_ORDER + q / kHeads;
+        uint64_t x = 0;
+#pragma unroll
+        for (int k = 0; k < order; ++k) x ^= w[k] * P.h.mult[mb + q * ENGRAM_MAX_ORDER + k];
+        if (POW2)
+            a[q] = static_cast<uint32_t>(x & (P.h.rows[s0 + q] - 1u));
+        else
+            a[q] = mod_rows(x, P.h.rows[s0 + q], P.h.magic[s0 + q]);
+    }
+
+    uint32_t v[kRowsPerModule];
+    float sc[kRowsPerModule];
+#pragma unroll
+    for (int q = 0; q < kRowsPerModule; ++q) {
+        const uint32_t* row =
+            reinterpret_cast<const uint32_t*>(P.g.tab[s0 + q] + static_cast<uint64_t>(a[q]) * kRowBytes);
+        v[q] = __builtin_nontemporal_load(row + lane);
+        sc[q] = P.g.sc[s0 + q][a[q]];
+    }
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < kRowsPerModule; ++q) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[q]), false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[q]), true);
+        acc.x = __builtin_fmaf(lo[0], sc[q], acc.x);
+        acc.y = __builtin_fmaf(lo[1], sc[q], acc.y);
+        acc.z = __builtin_fmaf(hi[0], sc[q], acc.z);
+        acc.w = __builtin_fmaf(hi[1], sc[q], acc.w);
+    }
+    __builtin_nontemporal_store(
+        acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + m * kRowBytes + lane * 4u));
+}
+
+}  // namespace
+
+hipError_t launch_lookup(const HashParams& h, const GatherParams& g, const int32_t* ids, const int32_t* history,
+                         uint32_t n_tok, uint32_t seq_len, float* out, hipStream_t stream) {
+    LookupParams p;
+    p.h = h;
+    p.g = g;
+    bool pow2 = true;
+    for (int s = 0; s < kSub; ++s) pow2 = pow2 && (h.rows[s] & (h.rows[s] - 1u)) == 0;
+    // Launches cover at most 2^24 tokens so the grid stays far below 2^32 threads.
+    constexpr uint32_t kChunk = 1u << 24;
+    for (uint32_t base = 0; base < n_tok; base += kChunk) {
+        const uint32_t n = min(kChunk, n_tok - base);
+        const uint32_t groups = ((n + 3u) / 4u + 3u) & ~3u;
+        const dim3 grid(2u * groups), block(256);
+        if (pow2)
+            hipLaunchKernelGGL(lookup_kernel<true>, grid, block, 0, stream, p, ids, history, base, base + n, seq_len,
+                               out);
+        else
+            hipLaunchKernelGGL(lookup_kernel<false>, grid, block, 0, stream, p, ids, history, base, base + n, seq_len,
+                               out);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace engram

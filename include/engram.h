@@ -178,6 +178,20 @@ int engram_gather_reduce(engram_plan_t plan, const uint32_t* addr, int64_t n_tok
                          const int32_t* n_unique, float* out, void* stream);
 
 /*
+ * Fused lookup: engram_hash followed by engram_gather_reduce (direct mode)
+ * in one launch, without the address buffer.  The addresses depend on the
+ * ids alone [VRAM; GUIDE "Engram"], so each (token, module) computes its own
+ * 24 rows and gathers them.  Bitwise identical to the two calls.
+ *
+ *   ids, history, n_seq, seq_len   as for engram_hash.
+ *   out       device fp32 [n_seq*seq_len][2][256], 16-byte aligned (output).
+ *
+ * n_seq*seq_len == 0 is a no-op.  Errors: EINVAL, ERANGE as engram_hash.
+ */
+int engram_lookup(engram_plan_t plan, const int32_t* ids, const int32_t* history,
+                  int64_t n_seq, int64_t seq_len, float* out, void* stream);
+
+/*
  * Workspace bytes engram_dedup needs for n_tok tokens (host-only).
  */
 int engram_dedup_workspace(int64_t n_tok, size_t* bytes);

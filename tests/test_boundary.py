@@ -220,3 +220,14 @@ def test_probe_validation(hg, plan):
     assert L.engram_probe_rows(plan, FAKE, -1, FAKE, None) == ERANGE
     assert L.engram_probe_rows(plan, FAKE, 0, FAKE, None) == OK
     assert L.engram_probe_rows(plan, FAKE, 1, FAKE + 4, None) == EINVAL
+
+
+def test_lookup_validation(hg, plan):
+    L = hg.lib()
+    assert L.engram_lookup(None, FAKE, None, 1, 1, FAKE, None) == EINVAL
+    assert L.engram_lookup(plan, FAKE, None, 0, 5, FAKE, None) == OK
+    assert L.engram_lookup(plan, FAKE, None, -1, 5, FAKE, None) == EINVAL
+    assert L.engram_lookup(plan, FAKE, None, 1 << 16, 1 << 15, FAKE, None) == ERANGE
+    assert L.engram_lookup(plan, None, None, 1, 1, FAKE, None) == EINVAL
+    assert L.engram_lookup(plan, FAKE, None, 1, 1, FAKE + 4, None) == EINVAL
+    assert L.engram_lookup(plan, FAKE, FAKE + 2, 1, 1, FAKE, None) == EINVAL

@@ -1,0 +1,102 @@
+"""Fused lookup (engram_lookup) against the two-call path and the oracle; HIP-graph replay."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_support import assert_within_tolerance, device_tables, lib, small_device_tables, to_dev_ids
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def test_fused_tiny_against_oracle():
+    w = workloads.WORKLOADS[1]
+    _say("fused lookup, tiny workload, all tokens vs oracle")
+    ids, hist = workloads.make_ids(w)
+    host_t, host_c = workloads.dense_tables(w.table_seed, w.rows)
+    t, c = small_device_tables(host_t, host_c)
+    plan = lib().Plan(t, c)
+    out = lib().lookup(plan, *to_dev_ids(ids, hist))
+    torch.cuda.synchronize()
+    _, want, abs_sum = oracle.lookup(ids, hist, host_t, host_c, [w.rows] * 48)
+    assert_within_tolerance(out.cpu().numpy(), want, abs_sum)
+
+
+@pytest.mark.parametrize("key", [2, 3, 4, 5])
+def test_fused_equals_two_calls_workloads(key):
+    w = workloads.WORKLOADS[key]
+    _say(f"fused == hash + gather, workload {key}")
+    ids, hist = workloads.make_ids(w)
+    t, c = device_tables(w.rows, w.table_seed)
+    plan = lib().Plan(t, c)
+    d_ids, d_hist = to_dev_ids(ids, hist)
+    two = lib().gather_reduce(plan, lib().hash(plan, d_ids, d_hist))
+    fused = torch.full_like(two, float("nan"))
+    lib().lookup(plan, d_ids, d_hist, out=fused)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two)
+
+
+@pytest.mark.parametrize("n_seq,seq_len,with_hist,rows", [
+    (1, 1, True, 1000003), (3, 5, True, 4099), (2, 333, False, 1 << 16), (5, 77, True, 65537), (1, 1, False, 1),
+])
+def test_fused_equals_two_calls_shapes(n_seq, seq_len, with_hist, rows):
+    _say(f"fused shapes {n_seq}x{seq_len} hist={with_hist} R={rows}")
+    rng = np.random.default_rng(rows + seq_len)
+    t, c = device_tables(rows, 3000 + rows % 1000)
+    plan = lib().Plan(t, c)
+    ids = rng.integers(0, 129280, size=(n_seq, seq_len)).astype(np.int32)
+    hist = rng.integers(0, 129280, size=(n_seq, 3)).astype(np.int32) if with_hist else None
+    d_ids, d_hist = to_dev_ids(ids, hist)
+    two = lib().gather_reduce(plan, lib().hash(plan, d_ids, d_hist))
+    fused = lib().lookup(plan, d_ids, d_hist)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two)
+
+
+def test_graph_replay_matches_eager():
+    """The stream-ordered calls capture into a HIP graph; every replay matches eager results."""
+    _say("hip graph capture and replay")
+    R = 4096
+    host_t, host_c = workloads.dense_tables(9, R)
+    t, c = small_device_tables(host_t, host_c)
+    plan = lib().Plan(t, c)
+    rng = np.random.default_rng(8)
+    ids_a = rng.integers(0, 129280, size=(64, 1)).astype(np.int32)
+    hist_a = rng.integers(0, 129280, size=(64, 3)).astype(np.int32)
+    d_ids, d_hist = to_dev_ids(ids_a, hist_a)
+    addr = torch.empty((64, 48), dtype=torch.uint32, device="cuda")
+    out = torch.empty((64, 2, 256), dtype=torch.float32, device="cuda")
+    out_f = torch.empty_like(out)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up on the side stream, as capture requires
+        lib().hash(plan, d_ids, d_hist, out=addr)
+        lib().gather_reduce(plan, addr, out=out)
+        lib().lookup(plan, d_ids, d_hist, out=out_f)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib().hash(plan, d_ids, d_hist, out=addr)
+        lib().gather_reduce(plan, addr, out=out)
+        lib().lookup(plan, d_ids, d_hist, out=out_f)
+    for rep in range(4):
+        new_ids = rng.integers(0, 129280, size=(64, 1)).astype(np.int32)
+        new_hist = rng.integers(0, 129280, size=(64, 3)).astype(np.int32)
+        d_ids.copy_(torch.from_numpy(new_ids))
+        d_hist.copy_(torch.from_numpy(new_hist))
+        out.zero_()
+        out_f.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = lib().gather_reduce(plan, lib().hash(plan, d_ids, d_hist))
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        assert torch.equal(out_f, eager), rep
+        _, want, abs_sum = oracle.lookup(new_ids, new_hist, host_t, host_c, [R] * 48)
+        assert_within_tolerance(out.cpu().numpy(), want, abs_sum)
