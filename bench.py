@@ -134,6 +134,8 @@ def main(argv=None) -> int:
                     help="synthetic workload (4: the full-size prefill the metric is quoted on)")
     ap.add_argument("--dedup", action="store_true", help="batched workloads: engram_dedup + dedup-mode gather")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the memory-ceiling probes")
+    ap.add_argument("--scale-format", default="f32_row", choices=["f32_row", "e8m0_block32"],
+                    help="row scales: one fp32 per row, or 8 E8M0 bytes per row (one per 32 elements)")
     ap.add_argument("--id-batches", type=int, default=1,
                     help="rotate among this many seeded id batches of the same shape (1: the workload's own ids)")
     args = ap.parse_args(argv)
@@ -155,10 +157,15 @@ def main(argv=None) -> int:
 
     _log(f"allocating 48 x {w.rows} x 256 B tables")
     tables = torch.empty((48, w.rows, 256), dtype=torch.uint8, device=dev)
-    scales = torch.empty((48, w.rows), dtype=torch.float32, device=dev)
-    hg.synth_fill(tables, scales, w.table_seed)
+    mx = args.scale_format == "e8m0_block32"
+    if mx:
+        scales = torch.empty((48, w.rows, 8), dtype=torch.uint8, device=dev)
+    else:
+        scales = torch.empty((48, w.rows), dtype=torch.float32, device=dev)
+    hg.synth_fill(tables, scales, w.table_seed, scale_format=args.scale_format)
     torch.cuda.synchronize()
-    plan = hg.Plan(tables, scales, vocab_size=workloads.VOCAB if w.ids_kind != "uniform1024" else 1024)
+    plan = hg.Plan(tables, scales, vocab_size=workloads.VOCAB if w.ids_kind != "uniform1024" else 1024,
+                   scale_format=args.scale_format)
 
     batches = []
     for b in range(args.id_batches):
@@ -227,14 +234,15 @@ def main(argv=None) -> int:
     ms_per_step = wall / args.steps * 1e3
     tok_s = n_tok / (ms_per_step / 1e3)
     n_unique = int(groups.n_unique.item()) if args.dedup else None
+    scale_bytes = 48 * (8 if mx else 4)  # per token
     if args.dedup:
         # one lookup per group (rows, scales, addresses, its offsets pair) + one perm read and one
         # 2 KiB output store per token
-        gather_bytes = n_unique * (48 * 256 + 48 * 4 + 48 * 4 + 8) + n_tok * (4 + 2 * 256 * 4)
+        gather_bytes = n_unique * (48 * 256 + scale_bytes + 48 * 4 + 8) + n_tok * (4 + 2 * 256 * 4)
     else:
-        gather_bytes = GATHER_BYTES_PER_TOKEN * n_tok
+        gather_bytes = (GATHER_BYTES_PER_TOKEN - 48 * 4 + scale_bytes) * n_tok
     achieved = gather_bytes / (gather_ms / 1e3) / 1e9
-    traffic = _traffic(n_tok) if args.workload == 4 and not args.dedup and args.id_batches == 1 else None
+    traffic = _traffic(n_tok) if args.workload == 4 and not args.dedup and args.id_batches == 1 and not mx else None
 
     base = None
     if args.cpu_sample > 0 and args.workload == 4:
@@ -258,6 +266,7 @@ def main(argv=None) -> int:
             "workload": (WORKLOAD_TEXT[args.workload]),
             "n_tok": n_tok,
             "rows_per_subtable": w.rows,
+            "scale_format": args.scale_format,
             "id_batches": args.id_batches,
             "step": "engram_hash + engram_dedup + engram_gather_reduce (dedup mode)" if args.dedup
                     else "engram_hash + engram_gather_reduce",

@@ -26,6 +26,9 @@ N_SUB = 48
 ROW_BYTES = 256
 N_MULT = 192
 DEFAULT_HASH_SEED = 0x454E4752414D0001
+SCALE_F32_ROW = 0
+SCALE_E8M0_BLOCK32 = 1
+_SCALE_FORMATS = {"f32_row": SCALE_F32_ROW, "e8m0_block32": SCALE_E8M0_BLOCK32}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libengram.so")
@@ -52,6 +55,8 @@ class PlanDesc(ctypes.Structure):
         ("rows", ctypes.POINTER(ctypes.c_uint64)),
         ("tables", ctypes.POINTER(ctypes.c_void_p)),
         ("scales", ctypes.POINTER(ctypes.c_void_p)),
+        ("scale_format", ctypes.c_uint32),
+        ("reserved1", ctypes.c_uint32),
     ]
 
 
@@ -71,6 +76,7 @@ def _load():
         "engram_dedup_workspace": [I64, ctypes.POINTER(ctypes.c_size_t)],
         "engram_dedup": [P, VP, VP, I64, I64, VP, VP, VP, VP, ctypes.c_size_t, VP],
         "engram_synth_fill": [VP, VP, U64, U32, U64, VP],
+        "engram_synth_fill_e8m0": [VP, U64, U32, U64, VP],
         "engram_probe_read": [VP, U64, VP, VP],
         "engram_probe_copy": [VP, VP, U64, VP],
         "engram_probe_rows": [P, VP, I64, VP, VP],
@@ -120,47 +126,55 @@ class Plan:
     """An immutable lookup plan over 48 device sub-tables.
 
     ``tables``: one uint8 tensor [48, R, 256] or a list of 48 tensors
-    [R_s, 256]; ``scales``: float32 [48, R] or a list of 48 tensors [R_s].
-    The tensors are referenced (not copied) and kept alive by the plan.
+    [R_s, 256]; ``scales``: float32 [48, R] / 48 x [R_s] ("f32_row"), or
+    uint8 [48, R, 8] / 48 x [R_s, 8] ("e8m0_block32").  The tensors are
+    referenced (not copied) and kept alive by the plan.
     """
 
-    def __init__(self, tables, scales, hash_seed: int = DEFAULT_HASH_SEED, vocab_size: int = 0):
+    def __init__(self, tables, scales, hash_seed: int = DEFAULT_HASH_SEED, vocab_size: int = 0,
+                 scale_format: str = "f32_row"):
+        if scale_format not in _SCALE_FORMATS:
+            raise ValueError(f"scale_format must be one of {sorted(_SCALE_FORMATS)}")
+        mx = scale_format == "e8m0_block32"
         if isinstance(tables, torch.Tensor):
             if tables.dim() != 3 or tables.shape[0] != N_SUB or tables.shape[2] != ROW_BYTES:
                 raise ValueError("tables must be [48, R, 256]")
             tables = list(tables.unbind(0))
         if isinstance(scales, torch.Tensor):
-            if scales.dim() != 2 or scales.shape[0] != N_SUB:
-                raise ValueError("scales must be [48, R]")
+            if scales.dim() != (3 if mx else 2) or scales.shape[0] != N_SUB:
+                raise ValueError("scales must be [48, R, 8]" if mx else "scales must be [48, R]")
             scales = list(scales.unbind(0))
         if len(tables) != N_SUB or len(scales) != N_SUB:
             raise ValueError("need 48 tables and 48 scale vectors")
         rows = []
         for s in range(N_SUB):
             t, c = tables[s], scales[s]
-            if t.dim() != 2 or t.shape[1] != ROW_BYTES or c.dim() != 1 or c.shape[0] != t.shape[0]:
-                raise ValueError(f"sub-table {s}: need table [R, 256] and scales [R]")
+            want = (t.shape[0], 8) if mx else (t.shape[0],)
+            if t.dim() != 2 or t.shape[1] != ROW_BYTES or tuple(c.shape) != want:
+                raise ValueError(f"sub-table {s}: need table [R, 256] and scales {list(want)}")
             _dev(t, torch.uint8, f"tables[{s}]")
-            _dev(c, torch.float32, f"scales[{s}]")
+            _dev(c, torch.uint8 if mx else torch.float32, f"scales[{s}]")
             rows.append(t.shape[0])
         self._build(rows, [t.data_ptr() for t in tables], [c.data_ptr() for c in scales], hash_seed, vocab_size,
-                    keep=(tables, scales))
+                    keep=(tables, scales), scale_format=_SCALE_FORMATS[scale_format])
 
     @classmethod
     def from_pointers(cls, rows, table_ptrs, scale_ptrs, hash_seed: int = DEFAULT_HASH_SEED, vocab_size: int = 0,
-                      keep=None) -> "Plan":
+                      keep=None, scale_format: str = "f32_row") -> "Plan":
         """Plan over raw device pointers (48 each) with the given row counts; ``keep`` is held alive."""
         p = cls.__new__(cls)
-        p._build(list(rows), list(table_ptrs), list(scale_ptrs), hash_seed, vocab_size, keep)
+        p._build(list(rows), list(table_ptrs), list(scale_ptrs), hash_seed, vocab_size, keep,
+                 scale_format=_SCALE_FORMATS[scale_format])
         return p
 
-    def _build(self, rows, tab_ptrs, sc_ptrs, hash_seed, vocab_size, keep) -> None:
+    def _build(self, rows, tab_ptrs, sc_ptrs, hash_seed, vocab_size, keep, scale_format: int = SCALE_F32_ROW) -> None:
         if len(rows) != N_SUB or len(tab_ptrs) != N_SUB or len(sc_ptrs) != N_SUB:
             raise ValueError("need 48 row counts, table pointers and scale pointers")
         self._handle = None
         self.rows = rows
         self.hash_seed = hash_seed
         self.vocab_size = vocab_size
+        self.scale_format = scale_format
         self._keep = keep
         self._rows_c = (ctypes.c_uint64 * N_SUB)(*rows)
         self._tabs_c = (ctypes.c_void_p * N_SUB)(*tab_ptrs)
@@ -169,6 +183,7 @@ class Plan:
         _check(_lib.engram_plan_desc_init(ctypes.byref(desc)), "engram_plan_desc_init")
         desc.hash_seed = hash_seed
         desc.vocab_size = vocab_size
+        desc.scale_format = scale_format
         desc.rows = ctypes.cast(self._rows_c, ctypes.POINTER(ctypes.c_uint64))
         desc.tables = ctypes.cast(self._tabs_c, ctypes.POINTER(ctypes.c_void_p))
         desc.scales = ctypes.cast(self._scs_c, ctypes.POINTER(ctypes.c_void_p))
@@ -298,23 +313,32 @@ def dedup(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, wo
     return groups
 
 
-def synth_fill(tables, scales, seed: int, stream=None) -> None:
-    """Fill 48 sub-tables from the seeded generator (engram_synth_fill).
+def synth_fill(tables, scales, seed: int, stream=None, scale_format: str = "f32_row") -> None:
+    """Fill 48 sub-tables from the seeded generator (engram_synth_fill, engram_synth_fill_e8m0).
 
     ``tables``: uint8 [48, R, 256] or a list of 48 [R, 256]; ``scales``:
-    float32 [48, R] or a list of 48 [R].
+    float32 [48, R] / 48 x [R] ("f32_row") or uint8 [48, R, 8] / 48 x [R, 8]
+    ("e8m0_block32").
     """
+    mx = _SCALE_FORMATS[scale_format] == SCALE_E8M0_BLOCK32
     tables = list(tables.unbind(0)) if isinstance(tables, torch.Tensor) else list(tables)
     scales = list(scales.unbind(0)) if isinstance(scales, torch.Tensor) else list(scales)
     if len(tables) != N_SUB or len(scales) != N_SUB:
         raise ValueError("need 48 tables and 48 scale vectors")
     for s in range(N_SUB):
         t, c = tables[s], scales[s]
-        if t.dim() != 2 or t.shape[1] != ROW_BYTES or tuple(c.shape) != (t.shape[0],):
-            raise ValueError(f"sub-table {s}: need table [R, 256] and scales [R]")
-        st = _lib.engram_synth_fill(_dev(t, torch.uint8, "table"), _dev(c, torch.float32, "scales"), t.shape[0], s,
-                                    seed, _stream(stream))
-        _check(st, "engram_synth_fill")
+        want = (t.shape[0], 8) if mx else (t.shape[0],)
+        if t.dim() != 2 or t.shape[1] != ROW_BYTES or tuple(c.shape) != want:
+            raise ValueError(f"sub-table {s}: need table [R, 256] and scales {list(want)}")
+        if mx:
+            st = _lib.engram_synth_fill(_dev(t, torch.uint8, "table"), None, t.shape[0], s, seed, _stream(stream))
+            _check(st, "engram_synth_fill")
+            st = _lib.engram_synth_fill_e8m0(_dev(c, torch.uint8, "scales"), t.shape[0], s, seed, _stream(stream))
+            _check(st, "engram_synth_fill_e8m0")
+        else:
+            st = _lib.engram_synth_fill(_dev(t, torch.uint8, "table"), _dev(c, torch.float32, "scales"), t.shape[0],
+                                        s, seed, _stream(stream))
+            _check(st, "engram_synth_fill")
 
 
 # ---------------------------------------------------------------------------

@@ -57,11 +57,15 @@ int engram_plan(const engram_plan_desc* d, engram_plan_t* out) {
         d->row_bytes != ENGRAM_ROW_BYTES)
         return ENGRAM_EUNSUPPORTED;
     if (!d->rows || !d->tables || !d->scales) return ENGRAM_EINVAL;
+    if (d->scale_format != ENGRAM_SCALE_F32_ROW && d->scale_format != ENGRAM_SCALE_E8M0_BLOCK32)
+        return ENGRAM_EUNSUPPORTED;
+    if (d->reserved1 != 0) return ENGRAM_EINVAL;
+    const uintptr_t scale_align = d->scale_format == ENGRAM_SCALE_F32_ROW ? 4 : 8;
     for (int s = 0; s < kSub; ++s) {
         const uint64_t r = d->rows[s];
         if (r == 0 || r > (uint64_t(1) << 32)) return ENGRAM_ERANGE;
         if (!d->tables[s] || !d->scales[s]) return ENGRAM_EINVAL;
-        if (!aligned(d->tables[s], 16) || !aligned(d->scales[s], 4)) return ENGRAM_EINVAL;
+        if (!aligned(d->tables[s], 16) || !aligned(d->scales[s], scale_align)) return ENGRAM_EINVAL;
     }
     engram_plan_s* p = new (std::nothrow) engram_plan_s;
     if (!p) return ENGRAM_EINVAL;
@@ -76,6 +80,7 @@ int engram_plan(const engram_plan_desc* d, engram_plan_t* out) {
         p->gather.tab[s] = d->tables[s];
         p->gather.sc[s] = d->scales[s];
     }
+    p->gather.scale_format = d->scale_format;
     *out = p;
     return ENGRAM_OK;
 }

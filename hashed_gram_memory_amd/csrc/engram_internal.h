@@ -22,10 +22,13 @@ struct HashParams {
     uint64_t magic[kSub];  // floor((2^64 - 1) / R_s): exact x mod R_s with one correction
 };
 
-// Row and scale base pointers of the 48 sub-tables, by value.
+// Row and scale base pointers of the 48 sub-tables, by value.  sc[s] points
+// at fp32 [R_s] or at uint8 [R_s][8] (E8M0 per 32-element block), as
+// scale_format says.
 struct GatherParams {
     const uint8_t* tab[kSub];
-    const float* sc[kSub];
+    const void* sc[kSub];
+    uint32_t scale_format;
 };
 
 }  // namespace engram

@@ -14,7 +14,8 @@
 //   * one wavefront per (token, module); a row is one coalesced
 //     global_load_dword of 64 lanes x 4 B, lane l holding elements 4l..4l+3;
 //   * the 24 addresses of a (token, module) are contiguous and wave-uniform
-//     (scalar loads), as are the 24 row bases and the 24 scales;
+//     (scalar loads), as are the 24 row bases and the 24 scales (or, with
+//     block scales, the 24 rows' 8-byte scale groups);
 //   * all 24 row loads are issued before the first is consumed, so a wave
 //     keeps 24 x 256 B in flight; with up to 8 waves per SIMD that is
 //     ~200 KB in flight per CU;
@@ -23,48 +24,19 @@
 //     reused rows and for the scale lines (every 4-byte scale read fetches a
 //     whole 128-byte line on gfx950);
 //   * decode with the gfx950 packed FP8 (OCP E4M3) -> fp32 conversion, then
-//     fused multiply-add into 4 fp32 accumulators per lane in ascending q;
+//     fused multiply-add into 4 fp32 accumulators per lane in ascending q
+//     (row_sum.h, shared with the fused lookup);
 //   * the 1 KiB result is written with non-temporal stores so output
 //     traffic does not evict table rows from L2 / MALL;
 //   * XCD-aware block order: the dispatcher hands block b to XCD b % 8; the
 //     grid is laid out so XCDs 0-3 serve module 0 and XCDs 4-7 module 1,
 //     which halves the set of sub-tables each XCD's L2 has to cache.
-#include "engram_internal.h"
+#include "row_sum.h"
 
 namespace engram {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Sum of the 24 dequantised rows of module m (wave-uniform) for one token;
-// `a` points at the token's 48 addresses.
-__device__ __forceinline__ f32x4 module_sum(const GatherParams& P, const uint32_t* __restrict__ a, uint32_t m,
-                                            uint32_t lane) {
-    uint32_t v[kRowsPerModule];
-    float sc[kRowsPerModule];
-    const uint32_t s0 = m * kRowsPerModule;
-#pragma unroll
-    for (int q = 0; q < kRowsPerModule; ++q) {
-        const uint32_t r = a[s0 + q];
-        const uint32_t* row =
-            reinterpret_cast<const uint32_t*>(P.tab[s0 + q] + static_cast<uint64_t>(r) * kRowBytes);
-        v[q] = __builtin_nontemporal_load(row + lane);
-        sc[q] = P.sc[s0 + q][r];
-    }
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int q = 0; q < kRowsPerModule; ++q) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[q]), false);  // bytes 0, 1
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[q]), true);   // bytes 2, 3
-        acc.x = __builtin_fmaf(lo[0], sc[q], acc.x);
-        acc.y = __builtin_fmaf(lo[1], sc[q], acc.y);
-        acc.z = __builtin_fmaf(hi[0], sc[q], acc.z);
-        acc.w = __builtin_fmaf(hi[1], sc[q], acc.w);
-    }
-    return acc;
-}
-
-template <bool kDedup>
+template <bool kDedup, int FMT>
 __global__ __launch_bounds__(256) void gather_reduce_kernel(const GatherParams P, const uint32_t* __restrict__ addr,
                                                             uint32_t item_base, uint32_t n_items,
                                                             const int32_t* __restrict__ perm,
@@ -85,8 +57,12 @@ __global__ __launch_bounds__(256) void gather_reduce_kernel(const GatherParams P
 
     uint32_t tok = item;
     if (kDedup) tok = static_cast<uint32_t>(perm[offsets[item]]);
-    const uint32_t* a = addr + static_cast<size_t>(tok) * kSub;
-    const f32x4 acc = module_sum(P, a, module, lane);
+    const uint32_t s0 = module * kRowsPerModule;
+    const uint32_t* ta = addr + static_cast<size_t>(tok) * kSub + s0;  // the module's 24 addresses
+    uint32_t a[kRowsPerModule];
+#pragma unroll
+    for (int q = 0; q < kRowsPerModule; ++q) a[q] = ta[q];
+    const f32x4 acc = sum_rows<FMT>(P, s0, a, lane);
 
     const size_t col = static_cast<size_t>(module) * kRowBytes + lane * 4u;
     if (!kDedup) {
@@ -100,6 +76,13 @@ __global__ __launch_bounds__(256) void gather_reduce_kernel(const GatherParams P
     }
 }
 
+template <bool kDedup, int FMT>
+void launch_one(const GatherParams& p, dim3 grid, hipStream_t stream, const uint32_t* addr, uint32_t base, uint32_t end,
+                const int32_t* perm, const int32_t* offsets, const int32_t* n_unique, float* out) {
+    hipLaunchKernelGGL((gather_reduce_kernel<kDedup, FMT>), grid, dim3(256), 0, stream, p, addr, base, end, perm, offsets,
+                       n_unique, out);
+}
+
 }  // namespace
 
 hipError_t launch_gather_reduce(const GatherParams& p, const uint32_t* addr, uint32_t n_tok, const int32_t* perm,
@@ -109,16 +92,19 @@ hipError_t launch_gather_reduce(const GatherParams& p, const uint32_t* addr, uin
     // Launches cover at most 2^24 items so the grid stays far below 2^32
     // threads.
     constexpr uint32_t kChunk = 1u << 24;
+    const bool mx = p.scale_format == ENGRAM_SCALE_E8M0_BLOCK32;
     for (uint32_t base = 0; base < n_tok; base += kChunk) {
         const uint32_t n = min(kChunk, n_tok - base);
         const uint32_t groups = ((n + 3u) / 4u + 3u) & ~3u;
-        const dim3 grid(2u * groups), block(256);
-        if (perm)
-            hipLaunchKernelGGL(gather_reduce_kernel<true>, grid, block, 0, stream, p, addr, base, base + n, perm,
-                               offsets, n_unique, out);
+        const dim3 grid(2u * groups);
+        if (perm && mx)
+            launch_one<true, ENGRAM_SCALE_E8M0_BLOCK32>(p, grid, stream, addr, base, base + n, perm, offsets, n_unique, out);
+        else if (perm)
+            launch_one<true, ENGRAM_SCALE_F32_ROW>(p, grid, stream, addr, base, base + n, perm, offsets, n_unique, out);
+        else if (mx)
+            launch_one<false, ENGRAM_SCALE_E8M0_BLOCK32>(p, grid, stream, addr, base, base + n, perm, offsets, n_unique, out);
         else
-            hipLaunchKernelGGL(gather_reduce_kernel<false>, grid, block, 0, stream, p, addr, base, base + n, perm,
-                               offsets, n_unique, out);
+            launch_one<false, ENGRAM_SCALE_F32_ROW>(p, grid, stream, addr, base, base + n, perm, offsets, n_unique, out);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

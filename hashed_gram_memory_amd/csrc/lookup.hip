@@ -14,12 +14,10 @@
 // multiply-xor and modulus as hash_kernel, and the accumulation the same
 // fused multiply-add sequence as gather_reduce_kernel, so the result is
 // bitwise identical to engram_hash followed by engram_gather_reduce.
-#include "engram_internal.h"
+#include "row_sum.h"
 
 namespace engram {
 namespace {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct LookupParams {
     HashParams h;
@@ -33,7 +31,7 @@ __device__ __forceinline__ uint32_t mod_rows(uint64_t x, uint64_t R, uint64_t ma
     return static_cast<uint32_t>(r);
 }
 
-template <bool POW2>
+template <bool POW2, int FMT>
 __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const int32_t* __restrict__ ids,
                                                      const int32_t* __restrict__ history, uint32_t tok_base,
                                                      uint32_t n_tok, uint32_t seq_len, float* __restrict__ out) {
@@ -77,25 +75,11 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
             a[q] = mod_rows(x, P.h.rows[s0 + q], P.h.magic[s0 + q]);
     }
 
-    uint32_t v[kRowsPerModule];
-    float sc[kRowsPerModule];
-#pragma unroll
-    for (int q = 0; q < kRowsPerModule; ++q) {
-        const uint32_t* row =
-            reinterpret_cast<const uint32_t*>(P.g.tab[s0 + q] + static_cast<uint64_t>(a[q]) * kRowBytes);
-        v[q] = __builtin_nontemporal_load(row + lane);
-        sc[q] = P.g.sc[s0 + q][a[q]];
-    }
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int q = 0; q < kRowsPerModule; ++q) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[q]), false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[q]), true);
-        acc.x = __builtin_fmaf(lo[0], sc[q], acc.x);
-        acc.y = __builtin_fmaf(lo[1], sc[q], acc.y);
-        acc.z = __builtin_fmaf(hi[0], sc[q], acc.z);
-        acc.w = __builtin_fmaf(hi[1], sc[q], acc.w);
-    }
+    // All 24 addresses are final before any row or scale is requested: the
+    // multipliers are scalar loads too, and a scalar-load wait would
+    // otherwise also wait for the (HBM-latency) scale loads issued so far.
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x4 acc = sum_rows<FMT, true>(P.g, s0, a, lane);
     __builtin_nontemporal_store(
         acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + m * kRowBytes + lane * 4u));
 }
@@ -111,16 +95,23 @@ hipError_t launch_lookup(const HashParams& h, const GatherParams& g, const int32
     for (int s = 0; s < kSub; ++s) pow2 = pow2 && (h.rows[s] & (h.rows[s] - 1u)) == 0;
     // Launches cover at most 2^24 tokens so the grid stays far below 2^32 threads.
     constexpr uint32_t kChunk = 1u << 24;
+    const bool mx = g.scale_format == ENGRAM_SCALE_E8M0_BLOCK32;
     for (uint32_t base = 0; base < n_tok; base += kChunk) {
         const uint32_t n = min(kChunk, n_tok - base);
         const uint32_t groups = ((n + 3u) / 4u + 3u) & ~3u;
         const dim3 grid(2u * groups), block(256);
-        if (pow2)
-            hipLaunchKernelGGL(lookup_kernel<true>, grid, block, 0, stream, p, ids, history, base, base + n, seq_len,
-                               out);
+        if (pow2 && mx)
+            hipLaunchKernelGGL((lookup_kernel<true, ENGRAM_SCALE_E8M0_BLOCK32>), grid, block, 0, stream, p, ids, history,
+                               base, base + n, seq_len, out);
+        else if (pow2)
+            hipLaunchKernelGGL((lookup_kernel<true, ENGRAM_SCALE_F32_ROW>), grid, block, 0, stream, p, ids, history, base,
+                               base + n, seq_len, out);
+        else if (mx)
+            hipLaunchKernelGGL((lookup_kernel<false, ENGRAM_SCALE_E8M0_BLOCK32>), grid, block, 0, stream, p, ids,
+                               history, base, base + n, seq_len, out);
         else
-            hipLaunchKernelGGL(lookup_kernel<false>, grid, block, 0, stream, p, ids, history, base, base + n, seq_len,
-                               out);
+            hipLaunchKernelGGL((lookup_kernel<false, ENGRAM_SCALE_F32_ROW>), grid, block, 0, stream, p, ids, history,
+                               base, base + n, seq_len, out);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -56,6 +56,22 @@ __global__ __launch_bounds__(256) void fill_scales_kernel(float* __restrict__ sc
     }
 }
 
+// Eight E8M0 exponents per row from the 8 bytes of one generator output.
+__global__ __launch_bounds__(256) void fill_e8m0_kernel(uint2* __restrict__ sc, uint64_t rows, uint64_t sub,
+                                                        uint64_t seed) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t r = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; r < rows; r += stride) {
+        const uint64_t z = splitmix_at(seed, (uint64_t(3) << 62) | (sub << 40) | r);
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const uint32_t u = static_cast<uint32_t>(z >> (8 * b)) & 0xFFu;
+            w[b >> 2] |= (120u + ((u * 15u) >> 8)) << (8 * (b & 3));
+        }
+        sc[r] = make_uint2(w[0], w[1]);
+    }
+}
+
 }  // namespace
 }  // namespace engram
 
@@ -74,4 +90,13 @@ extern "C" int engram_synth_fill(uint8_t* table, float* scales, uint64_t rows, u
     if (scales) hipLaunchKernelGGL(fill_scales_kernel, grid, block, 0, s, scales, rows, uint64_t(sub_index), seed);
     if (hipGetLastError() != hipSuccess) return ENGRAM_EHIP;
     return ENGRAM_OK;
+}
+
+extern "C" int engram_synth_fill_e8m0(uint8_t* scales, uint64_t rows, uint32_t sub_index, uint64_t seed, void* stream) {
+    using namespace engram;
+    if (rows == 0 || rows > (uint64_t(1) << 32)) return ENGRAM_ERANGE;
+    if (sub_index >= static_cast<uint32_t>(kSub) || !scales || !aligned(scales, 8)) return ENGRAM_EINVAL;
+    hipLaunchKernelGGL(fill_e8m0_kernel, dim3(2048), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       reinterpret_cast<uint2*>(scales), rows, uint64_t(sub_index), seed);
+    return hipGetLastError() == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
 }

@@ -57,6 +57,10 @@ extern "C" {
 #define ENGRAM_ROW_BYTES 256      /* FP8 E4M3 codes per row = output width       */
 #define ENGRAM_N_MULT 192         /* hash multipliers: 2 x 3 x 8 x 4             */
 
+/* Row scale formats (engram_plan_desc.scale_format). */
+#define ENGRAM_SCALE_F32_ROW 0       /* one fp32 scale per row                          */
+#define ENGRAM_SCALE_E8M0_BLOCK32 1  /* 8 E8M0 bytes per row, one per 32 elements      */
+
 /* Seed of the default hash multipliers: the bytes "ENGRAM" followed by 0x0001. */
 #define ENGRAM_DEFAULT_HASH_SEED 0x454E4752414D0001ULL
 
@@ -90,7 +94,18 @@ typedef enum engram_status {
  *       Sub-table s as row-major uint8 [R_s][256] of FP8 E4M3 codes (OCP
  *       encoding: bias 7, no infinities, 0x7F/0xFF are NaN).  16-byte aligned.
  *   scales[48] (host array of device pointers, copied)
- *       fp32 [R_s]: the scale of each row.  4-byte aligned.
+ *       ENGRAM_SCALE_F32_ROW: fp32 [R_s], the scale of each row; 4-byte
+ *       aligned.
+ *       ENGRAM_SCALE_E8M0_BLOCK32: uint8 [R_s][8], the 8 bytes of scales a
+ *       row carries [GUIDE "Engram"], read as one E8M0 exponent per block of
+ *       32 elements (element j uses byte j/32; e stands for 2^(e-127), 255
+ *       is NaN), the microscaling form of FP8 named for these tables [X];
+ *       8-byte aligned.
+ *   scale_format
+ *       ENGRAM_SCALE_F32_ROW (0, the default) or ENGRAM_SCALE_E8M0_BLOCK32
+ *       (else ENGRAM_EUNSUPPORTED).
+ *   reserved1
+ *       Must be 0.
  *
  * The plan copies the description; the tables themselves are not copied and
  * must outlive every call that uses the plan.
@@ -105,7 +120,9 @@ typedef struct engram_plan_desc {
     uint64_t hash_seed;
     const uint64_t* rows;
     const uint8_t* const* tables;
-    const float* const* scales;
+    const void* const* scales;
+    uint32_t scale_format;
+    uint32_t reserved1;            /* must be 0 */
 } engram_plan_desc;
 
 typedef struct engram_plan_s* engram_plan_t;
@@ -155,8 +172,10 @@ int engram_hash(engram_plan_t plan, const int32_t* ids, const int32_t* history,
  * Gather, dequantise and sum [GUIDE "Engram"; REQ].
  *
  * For token tok, module m and element j:
- *     out[tok][m][j] = sum_{q=0..23} fp8(T_{24m+q}[a][j]) * scale_{24m+q}[a],
- *     a = addr[tok][24m+q]
+ *     out[tok][m][j] = sum_{q=0..23} fp8(T_{24m+q}[a][j]) * scale_{24m+q}(a, j),
+ *     a = addr[tok][24m+q],
+ * scale(a, j) = scales[a] (fp32 per row) or 2^(scales[a][j/32] - 127) (E8M0
+ * per 32-element block),
  * accumulated in fp32 in ascending q (fused multiply-add), starting at +0.
  *
  *   addr    device uint32 [n_tok][48] (as written by engram_hash); every

@@ -17,6 +17,9 @@
  *   scale of row r of sub-table s:
  *       z = out(seed, (1 << 63) | (s << 40) | r);
  *       scale = (2^22 + (((z >> 40) * 3) >> 2)) * 2^-23   (exact, in [0.5, 2))
+ *   E8M0 block scales of row r of sub-table s (8 bytes, block b = byte b):
+ *       z = out(seed, (3 << 62) | (s << 40) | r);
+ *       e_b = 120 + ((((z >> 8b) & 255) * 15) >> 8)      (2^-7 .. 2^7)
  */
 #ifndef ENGRAM_SYNTH_H
 #define ENGRAM_SYNTH_H
@@ -35,6 +38,12 @@ extern "C" {
  */
 int engram_synth_fill(uint8_t* table, float* scales, uint64_t rows, uint32_t sub_index,
                       uint64_t seed, void* stream);
+
+/*
+ * Fill the E8M0 block scales of sub-table `sub_index`: scales = device uint8
+ * [rows][8] (8-byte aligned).  Same range checks as engram_synth_fill.
+ */
+int engram_synth_fill_e8m0(uint8_t* scales, uint64_t rows, uint32_t sub_index, uint64_t seed, void* stream);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,10 @@ from the library.
 """
 from .engram_oracle import (  # noqa: F401
     DEFAULT_HASH_SEED,
+    BLOCK,
     E4M3_TABLE,
+    E8M0_TABLE,
+    SCALE_FORMATS,
     N_HEADS,
     N_MODULES,
     N_SUB,
@@ -16,10 +19,12 @@ from .engram_oracle import (  # noqa: F401
     WINDOW,
     dedup,
     e4m3_value,
+    e8m0_value,
     gather_reduce,
     hash_addresses,
     lookup,
     multipliers,
+    row_scales,
     splitmix64,
     sub_index,
     windows,

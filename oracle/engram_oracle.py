@@ -15,6 +15,8 @@ Sources (web pages; cited by title and section):
   never multiplied"
 * [REQ] "Running DeepSeek V4.1 Flash locally: the numbers beyond 552B",
   section "Backbone, Engram, and active parameters describe different scales"
+* [X] "How DeepSeek V4.1 Flash's 763B weights run on consumer GPUs" (the
+  repost names MXFP8 among the published Engram table widths)
 
 What the pages fix: per token, suffix n-grams of order 2, 3 and 4 of the id
 stream are hashed by 8 independent heads in each of two Engram modules, one
@@ -33,7 +35,9 @@ design notes):
 * sub-table order: s = 24*m + 8*(n-2) + h;
 * positions before the sequence start take the caller's history ids, else 0;
 * FP8 flavour: E4M3 in the OCP encoding (bias 7, one NaN pattern per sign,
-  no infinities); one fp32 scale per row;
+  no infinities); one fp32 scale per row, or -- for the pages' 8 bytes of
+  scales per row, read as the microscaling FP8 format the tables are named
+  in [X] -- one E8M0 exponent per 32-element block;
 * combination: the 24 dequantised rows of a module are summed.  The pages'
   learned gate needs trained weights and a hidden state and is not part of
   this operator.
@@ -42,7 +46,8 @@ Floating point here is float64.  For the synthetic tables (scales k * 2^-23
 with k < 2^24) every product code*scale is a multiple of 2^-32 below 2^10 in
 magnitude, so every partial sum of 24 of them is a multiple of 2^-32 below
 2^15: float64 holds it exactly and the result does not depend on the
-summation order.
+summation order.  The same holds for block scales 2^-7 .. 2^7 (products are
+multiples of 2^-16 below 2^16).
 """
 from __future__ import annotations
 
@@ -170,16 +175,38 @@ def e4m3_value(code: int) -> float:
 E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
 
 
+def e8m0_value(e: int) -> float:
+    """Value of an E8M0 scale byte: 2^(e - 127); the byte 255 is NaN (no sign, no mantissa)."""
+    return math.nan if e == 255 else 2.0 ** (e - 127)
+
+
+E8M0_TABLE = np.array([e8m0_value(e) for e in range(256)], dtype=np.float64)
+SCALE_FORMATS = ("f32_row", "e8m0_block32")
+BLOCK = 32  # elements per E8M0 scale
+
+
 # ---------------------------------------------------------------------------
 # Steps a3-a5: gather, dequantise, per-module sum
 # ---------------------------------------------------------------------------
 
-def gather_reduce(tables, scales, addr) -> tuple[np.ndarray, np.ndarray]:
+def row_scales(scales_s, a, scale_format: str) -> np.ndarray:
+    """Scale of every element of the rows a of one sub-table: float64 [len(a), 256]."""
+    if scale_format == "f32_row":
+        sc = np.asarray(scales_s)[a].astype(np.float64)                 # one per row
+        return np.repeat(sc[:, None], ROW_BYTES, axis=1)
+    if scale_format == "e8m0_block32":
+        e = np.asarray(scales_s)[a]                                     # [n, 8] bytes
+        return np.repeat(E8M0_TABLE[e], BLOCK, axis=1)                  # element j uses byte j // 32
+    raise ValueError(scale_format)
+
+
+def gather_reduce(tables, scales, addr, scale_format: str = "f32_row") -> tuple[np.ndarray, np.ndarray]:
     """Memory vector of each token: float64 out [n_tok, 2, 256] and abs_sum.
 
     For module m and element j: out[tok][m][j] = sum over the module's 24
-    sub-tables q of decode(T_{24m+q}[addr][j]) * scale_{24m+q}[addr]
-    [GUIDE "Engram"; REQ].  abs_sum is the same sum of absolute terms, the
+    sub-tables q of decode(T_{24m+q}[addr][j]) * scale_{24m+q}(addr, j)
+    [GUIDE "Engram"; REQ], with one fp32 scale per row or one E8M0 scale per
+    32-element block.  abs_sum is the same sum of absolute terms, the
     yardstick of the fp32 tolerance.
     """
     addr = np.asarray(addr)
@@ -191,17 +218,17 @@ def gather_reduce(tables, scales, addr) -> tuple[np.ndarray, np.ndarray]:
             s = ROWS_PER_MODULE * m + q
             a = addr[:, s].astype(np.int64)
             codes = np.asarray(tables[s])[a]                           # a3: [n_tok, 256] bytes
-            sc = np.asarray(scales[s])[a].astype(np.float64)            # a3: [n_tok]
-            terms = E4M3_TABLE[codes] * sc[:, None]                     # a4
+            sc = row_scales(scales[s], a, scale_format)                 # a3: [n_tok, 256]
+            terms = E4M3_TABLE[codes] * sc                              # a4
             out[:, m, :] += terms                                       # a5
             abs_sum[:, m, :] += np.abs(terms)
     return out, abs_sum
 
 
-def lookup(ids, history, tables, scales, rows, hash_seed: int = DEFAULT_HASH_SEED):
+def lookup(ids, history, tables, scales, rows, hash_seed: int = DEFAULT_HASH_SEED, scale_format: str = "f32_row"):
     """Whole path: windows, hash, gather-reduce.  Returns (addr, out, abs_sum)."""
     addr = hash_addresses(windows(ids, history), multipliers(hash_seed), rows)
-    out, abs_sum = gather_reduce(tables, scales, addr)
+    out, abs_sum = gather_reduce(tables, scales, addr, scale_format)
     return addr, out, abs_sum
 
 

@@ -29,18 +29,26 @@ def big_buffer():
     return tabs, scs
 
 
+@functools.lru_cache(maxsize=1)
+def big_e8m0_buffer():
+    """[48, 2^24, 8] E8M0 block scales (6 GiB), shared by the block-scale tests."""
+    return torch.empty((48, FULL_ROWS, 8), dtype=torch.uint8, device="cuda")
+
+
 _filled = {"key": None}
 
 
-def device_tables(rows: int, seed: int):
+def device_tables(rows: int, seed: int, scale_format: str = "f32_row"):
     """48 device sub-tables of ``rows`` rows filled from the seeded generator (lists of views)."""
     tabs, scs = big_buffer()
+    if scale_format == "e8m0_block32":
+        scs = big_e8m0_buffer()
     t = [tabs[s, :rows] for s in range(48)]
     c = [scs[s, :rows] for s in range(48)]
-    if _filled["key"] != (rows, seed):
-        lib().synth_fill(t, c, seed)
+    if _filled["key"] != (rows, seed, scale_format):
+        lib().synth_fill(t, c, seed, scale_format=scale_format)
         torch.cuda.synchronize()
-        _filled["key"] = (rows, seed)
+        _filled["key"] = (rows, seed, scale_format)
     return t, c
 
 
@@ -84,14 +92,14 @@ def sample_tokens(n_tok: int, k: int, seed: int, must=()) -> np.ndarray:
     return np.array(sorted(pick), dtype=np.int64)
 
 
-def oracle_sampled(ids, history, rows: int, seed: int, tokens: np.ndarray):
+def oracle_sampled(ids, history, rows: int, seed: int, tokens: np.ndarray, scale_format: str = "f32_row"):
     """Oracle addresses for all tokens and memory vectors for ``tokens`` (regenerated rows)."""
     addr = oracle.hash_addresses(oracle.windows(ids, history), oracle.multipliers(), [rows] * 48)
     sub = addr[tokens]
-    host = workloads.SparseHostTables(seed, rows)
+    host = workloads.SparseHostTables(seed, rows, scale_format)
     try:
         host.materialise(sub)
-        out, abs_sum = oracle.gather_reduce(host.tables, host.scales, sub)
+        out, abs_sum = oracle.gather_reduce(host.tables, host.scales, sub, scale_format)
     finally:
         host.close()
     return addr, out, abs_sum

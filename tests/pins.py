@@ -299,3 +299,54 @@ def check_dedup(dedup_fn):
     win = np.array([[5, 0, 0, 0], [1 << 30, 0, 0, 0], [5, 0, 0, 1], [0, 9, 9, 9]], np.int64)
     perm, offsets, nu = dedup_fn(win)
     assert list(np.asarray(perm).tolist()) == [3, 0, 2, 1] and nu == 4
+
+
+# ---------------------------------------------------------------------------
+# E8M0 block scales
+# ---------------------------------------------------------------------------
+
+def check_e8m0(table):
+    """E8M0 decode against PyTorch's own float8_e8m0fnu conversion and the format's definition."""
+    import torch
+
+    table = np.asarray(table, dtype=np.float64)
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(table), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(table[ok], ref[ok])
+    assert table[127] == 1.0 and table[128] == 2.0 and table[126] == 0.5 and table[0] == 2.0 ** -127
+    assert np.isnan(table[255]) and np.isnan(table).sum() == 1
+
+
+def check_gather_reduce_e8m0(gr_fn):
+    """Block scales: closed forms that fix which byte scales which element."""
+    rng = np.random.default_rng(13)
+    R, N = 8, 30
+    addr = rng.integers(0, R, size=(N, N_SUB)).astype(np.uint32)
+    dec = _decode_ref()
+    # code 1.0 everywhere; byte b of every row = 127 + b - 3  -> element j = 24 * 2^(j//32 - 3)
+    tabs = [np.full((R, 256), 0x38, np.uint8) for _ in range(N_SUB)]
+    scs = [np.tile((124 + np.arange(8)).astype(np.uint8), (R, 1)) for _ in range(N_SUB)]
+    out, ab = gr_fn(tabs, scs, addr)
+    want = 24.0 * 2.0 ** (np.arange(256) // 32 - 3)
+    assert np.array_equal(out, np.broadcast_to(want, out.shape)) and np.array_equal(ab, out)
+    # one non-zero sub-table, random codes and exponents: element j = decode(code_j) * 2^(e[j//32]-127)
+    for s in (0, 13, 30, 47):
+        tabs = [np.zeros((R, 256), np.uint8) for _ in range(N_SUB)]
+        c = rng.integers(0, 254, size=(R, 256))
+        tabs[s] = np.where(c < 127, c, c + 1).astype(np.uint8)
+        scs = [rng.integers(110, 140, size=(R, 8)).astype(np.uint8) for _ in range(N_SUB)]
+        out, _ = gr_fn(tabs, scs, addr)
+        a = addr[:, s].astype(np.int64)
+        scale = 2.0 ** (scs[s][a].astype(np.float64) - 127)
+        want = dec[tabs[s][a]] * np.repeat(scale, 32, axis=1)
+        m = s // RPM
+        assert np.array_equal(out[:, m], want), s
+        assert not out[:, 1 - m].any()
+    # row index: a row's own exponents, not a neighbour's
+    tabs = [np.full((R, 256), 0x38, np.uint8) for _ in range(N_SUB)]
+    scs = [np.repeat((120 + np.arange(R)).astype(np.uint8)[:, None], 8, axis=1) for _ in range(N_SUB)]
+    out, _ = gr_fn(tabs, scs, addr)
+    for m in range(2):
+        want = sum(2.0 ** (120 + addr[:, RPM * m + q].astype(np.float64) - 127) for q in range(RPM))
+        assert np.array_equal(out[:, m, 0], want)

@@ -231,3 +231,25 @@ def test_lookup_validation(hg, plan):
     assert L.engram_lookup(plan, None, None, 1, 1, FAKE, None) == EINVAL
     assert L.engram_lookup(plan, FAKE, None, 1, 1, FAKE + 4, None) == EINVAL
     assert L.engram_lookup(plan, FAKE, FAKE + 2, 1, 1, FAKE, None) == EINVAL
+
+
+def test_plan_scale_formats(hg):
+    L = hg.lib()
+    d, keep = _desc(hg, scs=[FAKE + 8 * s for s in range(48)])
+    d.scale_format = 1
+    st, h = _plan(hg, d)
+    assert st == OK
+    L.engram_plan_destroy(h)
+    d, keep = _desc(hg, scs=[FAKE + 4 + 8 * s for s in range(48)])
+    d.scale_format = 1
+    assert _plan(hg, d)[0] == EINVAL  # block scales must be 8-byte aligned
+    d, keep = _desc(hg)
+    d.scale_format = 2
+    assert _plan(hg, d)[0] == EUNSUPPORTED
+    d, keep = _desc(hg)
+    d.reserved1 = 1
+    assert _plan(hg, d)[0] == EINVAL
+    assert L.engram_synth_fill_e8m0(FAKE, 0, 0, 1, None) == ERANGE
+    assert L.engram_synth_fill_e8m0(FAKE + 4, 16, 0, 1, None) == EINVAL
+    assert L.engram_synth_fill_e8m0(FAKE, 16, 48, 1, None) == EINVAL
+    assert L.engram_synth_fill_e8m0(None, 16, 0, 1, None) == EINVAL

@@ -266,3 +266,45 @@ def test_real_oracle_passes_every_pin():
     pins.check_multipliers(oracle.multipliers)
     pins.check_decode(oracle.E4M3_TABLE)
     pins.check_dedup(oracle.dedup)
+
+
+# --------------------------------------------------------------------------- E8M0 block scales
+
+def _gr_e8m0_variant(block=32, bias=127, byte_of=lambda j, blk: j // blk):
+    def gr(tables, scales, addr):
+        addr = np.asarray(addr)
+        n = addr.shape[0]
+        out = np.zeros((n, 2, 256))
+        ab = np.zeros((n, 2, 256))
+        j = np.arange(256)
+        for m in range(2):
+            for q in range(24):
+                s = 24 * m + q
+                a = addr[:, s].astype(np.int64)
+                e = np.asarray(scales[s])[a][:, np.minimum(byte_of(j, block), 7)].astype(np.float64)
+                t = eo.E4M3_TABLE[np.asarray(tables[s])[a]] * 2.0 ** (e - bias)
+                out[:, m] += t
+                ab[:, m] += np.abs(t)
+        return out, ab
+    return gr
+
+
+E8M0_MUTANTS = {
+    "block_16": _gr_e8m0_variant(block=16),
+    "block_64": _gr_e8m0_variant(block=64),
+    "bias_128": _gr_e8m0_variant(bias=128),
+    "bytes_reversed": _gr_e8m0_variant(byte_of=lambda j, blk: 7 - j // blk),
+    "byte_by_lane_mod": _gr_e8m0_variant(byte_of=lambda j, blk: (j // 4) % 8),
+}
+
+
+@pytest.mark.parametrize("name", sorted(E8M0_MUTANTS))
+def test_e8m0_mutants_caught(name):
+    assert _fails(pins.check_gather_reduce_e8m0, E8M0_MUTANTS[name])
+
+
+def test_e8m0_decode_mutants_caught():
+    bias128 = np.array([math.nan if e == 255 else 2.0 ** (e - 128) for e in range(256)])
+    no_nan = np.array([2.0 ** (e - 127) for e in range(256)])
+    assert _fails(pins.check_e8m0, bias128)
+    assert _fails(pins.check_e8m0, no_nan)

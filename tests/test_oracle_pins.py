@@ -104,3 +104,17 @@ def test_oracle_is_exact_in_float64():
     rev_a = np.stack([addr[:, 24 * (s // 24) + 23 - s % 24] for s in range(48)], axis=1)
     out2, _ = oracle.gather_reduce(rev_t, rev_s, rev_a)
     assert np.array_equal(out, out2)
+
+
+def test_e8m0_decode_against_torch():
+    pins.check_e8m0(oracle.E8M0_TABLE)
+
+
+def test_gather_reduce_e8m0_closed_forms():
+    pins.check_gather_reduce_e8m0(lambda t, s, a: oracle.gather_reduce(t, s, a, "e8m0_block32"))
+
+
+def test_scale_format_rejected():
+    with pytest.raises(ValueError):
+        oracle.gather_reduce([np.zeros((1, 256), np.uint8)] * 48, [np.ones(1, np.float32)] * 48,
+                             np.zeros((1, 48), np.uint32), "bf16")

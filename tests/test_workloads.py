@@ -69,3 +69,15 @@ def test_sparse_host_tables_hold_requested_rows():
         assert np.array_equal(t.tables[s][addr[:, s].astype(np.int64)], c)
         assert np.array_equal(t.scales[s][addr[:, s].astype(np.int64)], sc)
     t.close()
+
+
+def test_e8m0_generator():
+    e = workloads.e8m0_range(42, 5, 100, 3000)
+    assert e.shape == (3000, 8) and e.min() >= 120 and e.max() <= 134
+    assert len(np.unique(e)) == 15
+    assert np.array_equal(workloads.e8m0_rows(42, 5, np.arange(100, 3100)), e)
+    t = workloads.SparseHostTables(42, 1 << 20, "e8m0_block32")
+    addr = np.random.default_rng(1).integers(0, 1 << 20, size=(4, 48)).astype(np.uint32)
+    t.materialise(addr)
+    assert np.array_equal(t.scales[5][addr[:, 5].astype(np.int64)], workloads.e8m0_rows(42, 5, addr[:, 5]))
+    t.close()

@@ -155,6 +155,9 @@ def _tablegen():
         lib.tablegen_rows.argtypes = [ctypes.c_uint64, ctypes.c_uint32, p, ctypes.c_int64, p, p]
         lib.tablegen_scatter.argtypes = [ctypes.c_uint64, ctypes.c_uint32, p, ctypes.c_int64, p, p]
         lib.tablegen_range.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint64, p, p]
+        lib.tablegen_e8m0_rows.argtypes = [ctypes.c_uint64, ctypes.c_uint32, p, ctypes.c_int64, p]
+        lib.tablegen_e8m0_scatter.argtypes = [ctypes.c_uint64, ctypes.c_uint32, p, ctypes.c_int64, p]
+        lib.tablegen_e8m0_range.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint64, p]
         _lib = lib
     return _lib
 
@@ -179,13 +182,30 @@ def table_range(seed: int, s: int, r0: int, n: int) -> tuple[np.ndarray, np.ndar
     return codes, scales
 
 
-def dense_tables(seed: int, rows: int) -> tuple[list, list]:
-    """All 48 sub-tables in host memory (small row counts only)."""
+def e8m0_rows(seed: int, s: int, rows) -> np.ndarray:
+    """E8M0 block scales uint8 [n, 8] of the given rows of sub-table s."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint32)
+    out = np.empty((rows.size, 8), np.uint8)
+    _tablegen().tablegen_e8m0_rows(seed, s, _ptr(rows), rows.size, _ptr(out))
+    return out
+
+
+def e8m0_range(seed: int, s: int, r0: int, n: int) -> np.ndarray:
+    out = np.empty((n, 8), np.uint8)
+    _tablegen().tablegen_e8m0_range(seed, s, r0, n, _ptr(out))
+    return out
+
+
+def dense_tables(seed: int, rows: int, scale_format: str = "f32_row") -> tuple[list, list]:
+    """All 48 sub-tables in host memory (small row counts only).
+
+    ``scale_format`` "f32_row": scales float32 [rows]; "e8m0_block32": uint8 [rows, 8].
+    """
     tabs, scs = [], []
     for s in range(N_SUB):
         c, sc = table_range(seed, s, 0, rows)
         tabs.append(c)
-        scs.append(sc)
+        scs.append(sc if scale_format == "f32_row" else e8m0_range(seed, s, 0, rows))
     return tabs, scs
 
 
@@ -197,14 +217,17 @@ class SparseHostTables:
     resident memory is only the pages that hold requested rows.
     """
 
-    def __init__(self, seed: int, rows: int):
-        self.seed, self.rows = seed, rows
+    def __init__(self, seed: int, rows: int, scale_format: str = "f32_row"):
+        self.seed, self.rows, self.scale_format = seed, rows, scale_format
         nbytes = N_SUB * rows * ROW_BYTES
         flags = mmap.MAP_PRIVATE | mmap.MAP_ANONYMOUS | getattr(mmap, "MAP_NORESERVE", 0x4000)  # Linux value
         self._tab_map = mmap.mmap(-1, nbytes, flags=flags)
-        self._sc_map = mmap.mmap(-1, N_SUB * rows * 4, flags=flags)
+        self._sc_map = mmap.mmap(-1, N_SUB * rows * (4 if scale_format == "f32_row" else 8), flags=flags)
         tab = np.frombuffer(self._tab_map, dtype=np.uint8).reshape(N_SUB, rows, ROW_BYTES)
-        sc = np.frombuffer(self._sc_map, dtype=np.float32).reshape(N_SUB, rows)
+        if scale_format == "f32_row":
+            sc = np.frombuffer(self._sc_map, dtype=np.float32).reshape(N_SUB, rows)
+        else:
+            sc = np.frombuffer(self._sc_map, dtype=np.uint8).reshape(N_SUB, rows, 8)
         self.tables = [tab[s] for s in range(N_SUB)]
         self.scales = [sc[s] for s in range(N_SUB)]
 
@@ -213,8 +236,11 @@ class SparseHostTables:
         addr = np.asarray(addr)
         for s in range(N_SUB):
             need = np.unique(addr[:, s]).astype(np.uint32)
+            f32 = self.scale_format == "f32_row"
             _tablegen().tablegen_scatter(self.seed, s, _ptr(need), need.size,
-                                         _ptr(self.tables[s]), _ptr(self.scales[s]))
+                                         _ptr(self.tables[s]), _ptr(self.scales[s]) if f32 else None)
+            if not f32:
+                _tablegen().tablegen_e8m0_scatter(self.seed, s, _ptr(need), need.size, _ptr(self.scales[s]))
 
     def close(self) -> None:
         self.tables = self.scales = None

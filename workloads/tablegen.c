@@ -22,6 +22,8 @@
  *   scales: idx = (1 << 63) | (s << 40) | r;
  *           k = 2^22 + (((out >> 40) * 3) >> 2);   scale = k * 2^-23
  *           (k < 2^24, so the scale is exact in fp32 and lies in [0.5, 2)).
+ *   E8M0 block scales (8 bytes per row): idx = (3 << 62) | (s << 40) | r;
+ *           byte b = 120 + (((out >> 8b) & 255) * 15 >> 8)   (2^-7 .. 2^7).
  */
 #include <stdint.h>
 #include <string.h>
@@ -83,4 +85,31 @@ void tablegen_range(uint64_t seed, uint32_t s, uint64_t r0, uint64_t n,
         if (codes) row_codes(seed, s, r0 + i, codes + i * 256);
         if (scales) scales[i] = row_scale(seed, s, r0 + i);
     }
+}
+
+static inline void row_e8m0(uint64_t seed, uint64_t s, uint64_t r, uint8_t *dst)
+{
+    uint64_t z = splitmix_at(seed, (3ull << 62) | (s << 40) | r);
+    for (int b = 0; b < 8; ++b) {
+        uint32_t u = (uint32_t)((z >> (8 * b)) & 0xFFu);
+        dst[b] = (uint8_t)(120u + ((u * 15u) >> 8));
+    }
+}
+
+/* E8M0 block scales: rows[i] -> out[i*8 ..] */
+void tablegen_e8m0_rows(uint64_t seed, uint32_t s, const uint32_t *rows, int64_t n, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) row_e8m0(seed, s, rows[i], out + i * 8);
+}
+
+/* Scatter form into a [R][8] array. */
+void tablegen_e8m0_scatter(uint64_t seed, uint32_t s, const uint32_t *rows, int64_t n, uint8_t *scales)
+{
+    for (int64_t i = 0; i < n; ++i) row_e8m0(seed, s, rows[i], scales + (uint64_t)rows[i] * 8u);
+}
+
+/* Contiguous range [r0, r0 + n) into out[n*8]. */
+void tablegen_e8m0_range(uint64_t seed, uint32_t s, uint64_t r0, uint64_t n, uint8_t *out)
+{
+    for (uint64_t i = 0; i < n; ++i) row_e8m0(seed, s, r0 + i, out + i * 8);
 }
