@@ -41,7 +41,16 @@ WORKLOAD_TEXT = {
         "sub-tables x 2^24 rows x 256 B FP8 E4M3 (192 GiB) + fp32 row scales"),
 }
 PMC_FILE = os.path.join(ROOT, "profiles", "gather_reduce_full_131072_pmc.json")
-GATHER_SRC = os.path.join(ROOT, "hashed_gram_memory_amd", "csrc", "gather_reduce.hip")
+# sources the gather kernel is compiled from (the counter summary is valid only for this exact code)
+GATHER_SRCS = [os.path.join(ROOT, "hashed_gram_memory_amd", "csrc", f)
+               for f in ("gather_reduce.hip", "row_sum.h", "engram_internal.h")]
+
+
+def gather_source_sha256() -> str:
+    h = hashlib.sha256()
+    for f in GATHER_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def _log(msg: str) -> None:
@@ -54,8 +63,7 @@ def _traffic(n_tok: int):
         rec = json.load(open(PMC_FILE))
     except (OSError, ValueError):
         return None
-    src = hashlib.sha256(open(GATHER_SRC, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != src or rec.get("n_tok") != n_tok:
+    if rec.get("kernel_source_sha256") != gather_source_sha256() or rec.get("n_tok") != n_tok:
         return None
     return rec.get("hbm_bytes_per_launch")
 

@@ -73,6 +73,8 @@ def _load():
         "engram_hash": [P, VP, VP, I64, I64, VP, VP],
         "engram_gather_reduce": [P, VP, I64, VP, VP, VP, VP, VP],
         "engram_lookup": [P, VP, VP, I64, I64, VP, VP],
+        "engram_gather_weighted": [P, VP, I64, VP, VP, VP],
+        "engram_gather_rows": [P, VP, I64, VP, VP],
         "engram_dedup_workspace": [I64, ctypes.POINTER(ctypes.c_size_t)],
         "engram_dedup": [P, VP, VP, I64, I64, VP, VP, VP, VP, ctypes.c_size_t, VP],
         "engram_synth_fill": [VP, VP, U64, U32, U64, VP],
@@ -282,6 +284,38 @@ def lookup(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, o
                             None if history is None else _dev(history, torch.int32, "history"), n_seq, seq_len,
                             _dev(out, torch.float32, "out"), _stream(stream))
     _check(st, "engram_lookup")
+    return out
+
+
+def gather_weighted(plan: Plan, addr: torch.Tensor, weights: torch.Tensor, out: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Per-module sum with one caller weight per row: fp32 [n_tok, 2, 256] (engram_gather_weighted)."""
+    if addr.dim() != 2 or addr.shape[1] != N_SUB or tuple(weights.shape) != tuple(addr.shape):
+        raise ValueError("addr and weights must be [n_tok, 48]")
+    n_tok = addr.shape[0]
+    if out is None:
+        out = torch.empty((n_tok, N_MODULES, ROW_BYTES), dtype=torch.float32, device=addr.device)
+    elif tuple(out.shape) != (n_tok, N_MODULES, ROW_BYTES):
+        raise ValueError("out must be [n_tok, 2, 256]")
+    st = _lib.engram_gather_weighted(plan.handle, _dev(addr, torch.uint32, "addr"), n_tok,
+                                     _dev(weights, torch.float32, "weights"), _dev(out, torch.float32, "out"),
+                                     _stream(stream))
+    _check(st, "engram_gather_weighted")
+    return out
+
+
+def gather_rows(plan: Plan, addr: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The 48 dequantised rows of every token: fp32 [n_tok, 48, 256] (engram_gather_rows)."""
+    if addr.dim() != 2 or addr.shape[1] != N_SUB:
+        raise ValueError("addr must be [n_tok, 48]")
+    n_tok = addr.shape[0]
+    if out is None:
+        out = torch.empty((n_tok, N_SUB, ROW_BYTES), dtype=torch.float32, device=addr.device)
+    elif tuple(out.shape) != (n_tok, N_SUB, ROW_BYTES):
+        raise ValueError("out must be [n_tok, 48, 256]")
+    st = _lib.engram_gather_rows(plan.handle, _dev(addr, torch.uint32, "addr"), n_tok, _dev(out, torch.float32, "rows"),
+                                 _stream(stream))
+    _check(st, "engram_gather_rows")
     return out
 
 

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libengram.so")
-SOURCES = ["engram_api.cpp", "hash.hip", "gather_reduce.hip", "dedup.hip", "synth_fill.hip", "probe.hip", "lookup.hip"]
+SOURCES = ["engram_api.cpp", "hash.hip", "gather_reduce.hip", "dedup.hip", "synth_fill.hip", "probe.hip", "lookup.hip", "gate_io.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.

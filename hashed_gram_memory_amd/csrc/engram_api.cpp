@@ -139,6 +139,26 @@ int engram_lookup(engram_plan_t p, const int32_t* ids, const int32_t* history, i
     return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
 }
 
+int engram_gather_weighted(engram_plan_t p, const uint32_t* addr, int64_t n_tok, const float* weights, float* out,
+                           void* stream) {
+    if (!valid_plan(p)) return ENGRAM_EINVAL;
+    if (n_tok < 0 || n_tok > kMaxTokens) return ENGRAM_ERANGE;
+    if (n_tok == 0) return ENGRAM_OK;
+    if (!addr || !weights || !out || !aligned(addr, 16) || !aligned(weights, 16) || !aligned(out, 16))
+        return ENGRAM_EINVAL;
+    hipError_t e = launch_gate_io(p->gather, addr, weights, uint32_t(n_tok), out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
+}
+
+int engram_gather_rows(engram_plan_t p, const uint32_t* addr, int64_t n_tok, float* rows, void* stream) {
+    if (!valid_plan(p)) return ENGRAM_EINVAL;
+    if (n_tok < 0 || n_tok > kMaxTokens) return ENGRAM_ERANGE;
+    if (n_tok == 0) return ENGRAM_OK;
+    if (!addr || !rows || !aligned(addr, 16) || !aligned(rows, 16)) return ENGRAM_EINVAL;
+    hipError_t e = launch_gate_io(p->gather, addr, nullptr, uint32_t(n_tok), rows, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
+}
+
 int engram_dedup_workspace(int64_t n_tok, size_t* bytes) {
     if (!bytes) return ENGRAM_EINVAL;
     if (n_tok < 0 || n_tok > kMaxTokens) return ENGRAM_ERANGE;

@@ -54,6 +54,11 @@ hipError_t launch_gather_reduce(const GatherParams& p, const uint32_t* addr, uin
 hipError_t launch_lookup(const HashParams& h, const GatherParams& g, const int32_t* ids, const int32_t* history,
                          uint32_t n_tok, uint32_t seq_len, float* out, hipStream_t stream);
 
+// weights != nullptr: weighted per-module sums into out [n_tok][2][256];
+// weights == nullptr: un-reduced rows into out [n_tok][48][256].
+hipError_t launch_gate_io(const GatherParams& p, const uint32_t* addr, const float* weights, uint32_t n_tok,
+                          float* out, hipStream_t stream);
+
 size_t dedup_workspace_bytes(uint32_t n_tok);
 
 uint32_t dedup_key_bits(uint32_t vocab_size);

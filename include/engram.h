@@ -197,6 +197,31 @@ int engram_gather_reduce(engram_plan_t plan, const uint32_t* addr, int64_t n_tok
                          const int32_t* n_unique, float* out, void* stream);
 
 /*
+ * Inputs for the learned gate that follows the lookup: each retrieved row is
+ * weighed against the hidden state before the module's rows are combined
+ * [GUIDE "The architecture", "Engram"].  The gate itself (trained weights,
+ * hidden states) is outside this library.
+ *
+ * engram_gather_weighted: as engram_gather_reduce (direct mode) with one
+ * caller weight per row:
+ *     out[tok][m][j] = sum_q fp8(T_{24m+q}[a][j]) * fp32(scale_{24m+q}(a, j) * w[tok][24m+q])
+ * accumulated in fp32 in ascending q; with every weight 1 the result is
+ * bitwise that of engram_gather_reduce.
+ *   weights  device fp32 [n_tok][48] (same order as addr), 16-byte aligned.
+ *   out      device fp32 [n_tok][2][256], 16-byte aligned (output).
+ *
+ * engram_gather_rows: the 48 dequantised rows of every token, un-reduced:
+ *     rows[tok][s][j] = fp32(fp8(T_s[a][j]) * scale_s(a, j)),  a = addr[tok][s]
+ *   rows     device fp32 [n_tok][48][256] (48 KiB per token), 16-byte aligned.
+ *
+ * n_tok == 0 is a no-op.  Errors: EINVAL (NULL/misaligned pointer), ERANGE.
+ */
+int engram_gather_weighted(engram_plan_t plan, const uint32_t* addr, int64_t n_tok,
+                           const float* weights, float* out, void* stream);
+int engram_gather_rows(engram_plan_t plan, const uint32_t* addr, int64_t n_tok, float* rows,
+                       void* stream);
+
+/*
  * Fused lookup: engram_hash followed by engram_gather_reduce (direct mode)
  * in one launch, without the address buffer.  The addresses depend on the
  * ids alone [VRAM; GUIDE "Engram"], so each (token, module) computes its own

@@ -21,6 +21,8 @@ from .engram_oracle import (  # noqa: F401
     e4m3_value,
     e8m0_value,
     gather_reduce,
+    gather_rows,
+    gather_weighted,
     hash_addresses,
     lookup,
     multipliers,

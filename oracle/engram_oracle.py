@@ -225,6 +225,31 @@ def gather_reduce(tables, scales, addr, scale_format: str = "f32_row") -> tuple[
     return out, abs_sum
 
 
+def gather_rows(tables, scales, addr, scale_format: str = "f32_row") -> np.ndarray:
+    """The 48 dequantised rows of each token, un-reduced: float64 [n_tok, 48, 256].
+
+    These are what the pages' learned gate weighs against the hidden state
+    [GUIDE "The architecture", "Engram"].
+    """
+    addr = np.asarray(addr)
+    rows = np.empty((addr.shape[0], N_SUB, ROW_BYTES), np.float64)
+    for s in range(N_SUB):
+        a = addr[:, s].astype(np.int64)
+        rows[:, s, :] = E4M3_TABLE[np.asarray(tables[s])[a]] * row_scales(scales[s], a, scale_format)
+    return rows
+
+
+def gather_weighted(tables, scales, addr, weights, scale_format: str = "f32_row") -> tuple[np.ndarray, np.ndarray]:
+    """Per-module sum with one weight per row: out[tok][m][j] = sum_q w[tok][24m+q] * row_{24m+q}[j].
+
+    Returns (out, abs_sum) in float64, abs_sum being the sum of |terms|.
+    """
+    rows = gather_rows(tables, scales, addr, scale_format)
+    terms = rows * np.asarray(weights, np.float64)[:, :, None]
+    t = terms.reshape(terms.shape[0], N_MODULES, ROWS_PER_MODULE, ROW_BYTES)
+    return t.sum(axis=2), np.abs(t).sum(axis=2)
+
+
 def lookup(ids, history, tables, scales, rows, hash_seed: int = DEFAULT_HASH_SEED, scale_format: str = "f32_row"):
     """Whole path: windows, hash, gather-reduce.  Returns (addr, out, abs_sum)."""
     addr = hash_addresses(windows(ids, history), multipliers(hash_seed), rows)

@@ -350,3 +350,37 @@ def check_gather_reduce_e8m0(gr_fn):
     for m in range(2):
         want = sum(2.0 ** (120 + addr[:, RPM * m + q].astype(np.float64) - 127) for q in range(RPM))
         assert np.array_equal(out[:, m, 0], want)
+
+
+# ---------------------------------------------------------------------------
+# gate inputs: un-reduced rows and caller-weighted sums
+# ---------------------------------------------------------------------------
+
+def check_gate_inputs(rows_fn, weighted_fn, gr_fn):
+    """Un-reduced rows and weighted sums against the plain sum and closed forms."""
+    rng = np.random.default_rng(17)
+    R, N = 32, 20
+    addr = rng.integers(0, R, size=(N, N_SUB)).astype(np.uint32)
+    c = rng.integers(0, 254, size=(N_SUB, R, 256))
+    tabs = [np.where(x < 127, x, x + 1).astype(np.uint8) for x in c]
+    scs = [(rng.integers(1 << 22, 1 << 24, size=R) * 2.0 ** -23).astype(np.float32) for _ in range(N_SUB)]
+    dec = _decode_ref()
+    rows = rows_fn(tabs, scs, addr)
+    assert rows.shape == (N, N_SUB, 256)
+    for s in (0, 11, 24, 47):  # each row is its own decode times its own scale
+        a = addr[:, s].astype(np.int64)
+        assert np.array_equal(rows[:, s], dec[tabs[s][a]] * scs[s][a].astype(np.float64)[:, None]), s
+    out, _ = gr_fn(tabs, scs, addr)
+    ones, _ = weighted_fn(tabs, scs, addr, np.ones((N, N_SUB)))
+    assert np.array_equal(ones, out)  # unit weights: the plain sum
+    assert np.array_equal(rows.reshape(N, 2, 24, 256).sum(axis=2), out)
+    w = np.zeros((N, N_SUB))
+    w[:, 5] = 1.0
+    w[:, 40] = -2.0
+    one, _ = weighted_fn(tabs, scs, addr, w)
+    assert np.array_equal(one[:, 0], rows[:, 5]) and np.array_equal(one[:, 1], -2.0 * rows[:, 40])
+    w = rng.uniform(-1, 1, size=(N, N_SUB))
+    got, ab = weighted_fn(tabs, scs, addr, w)
+    want = np.einsum("nsj,ns->nsj", rows, w).reshape(N, 2, 24, 256).sum(axis=2)
+    assert np.allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
+    assert np.all(ab >= np.abs(got) - 1e-9)

@@ -253,3 +253,16 @@ def test_plan_scale_formats(hg):
     assert L.engram_synth_fill_e8m0(FAKE + 4, 16, 0, 1, None) == EINVAL
     assert L.engram_synth_fill_e8m0(FAKE, 16, 48, 1, None) == EINVAL
     assert L.engram_synth_fill_e8m0(None, 16, 0, 1, None) == EINVAL
+
+
+def test_gate_io_validation(hg, plan):
+    L = hg.lib()
+    assert L.engram_gather_weighted(None, FAKE, 1, FAKE, FAKE, None) == EINVAL
+    assert L.engram_gather_weighted(plan, FAKE, 0, FAKE, FAKE, None) == OK
+    assert L.engram_gather_weighted(plan, FAKE, -1, FAKE, FAKE, None) == ERANGE
+    assert L.engram_gather_weighted(plan, FAKE, 1, None, FAKE, None) == EINVAL
+    assert L.engram_gather_weighted(plan, FAKE, 1, FAKE + 4, FAKE, None) == EINVAL
+    assert L.engram_gather_rows(None, FAKE, 1, FAKE, None) == EINVAL
+    assert L.engram_gather_rows(plan, FAKE, 0, FAKE, None) == OK
+    assert L.engram_gather_rows(plan, FAKE, 1, FAKE + 8, None) == EINVAL
+    assert L.engram_gather_rows(plan, FAKE, 1 << 31, FAKE, None) == ERANGE

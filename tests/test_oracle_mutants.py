@@ -308,3 +308,28 @@ def test_e8m0_decode_mutants_caught():
     no_nan = np.array([2.0 ** (e - 127) for e in range(256)])
     assert _fails(pins.check_e8m0, bias128)
     assert _fails(pins.check_e8m0, no_nan)
+
+
+# --------------------------------------------------------------------------- gate inputs
+
+def _rows_module_swapped(t, s, a, fmt="f32_row"):
+    r = eo.gather_rows(t, s, a, fmt)
+    return np.concatenate([r[:, 24:], r[:, :24]], axis=1)
+
+
+def _weighted_transposed(t, s, a, w, fmt="f32_row"):
+    w = np.asarray(w)
+    return eo.gather_weighted(t, s, a, w[:, ::-1], fmt)
+
+
+def _weighted_unweighted(t, s, a, w, fmt="f32_row"):
+    return eo.gather_reduce(t, s, a, fmt)
+
+
+@pytest.mark.parametrize("rows_fn,weighted_fn", [
+    (_rows_module_swapped, eo.gather_weighted),
+    (eo.gather_rows, _weighted_transposed),
+    (eo.gather_rows, _weighted_unweighted),
+])
+def test_gate_input_mutants_caught(rows_fn, weighted_fn):
+    assert _fails(pins.check_gate_inputs, rows_fn, weighted_fn, eo.gather_reduce)

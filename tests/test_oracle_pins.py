@@ -118,3 +118,7 @@ def test_scale_format_rejected():
     with pytest.raises(ValueError):
         oracle.gather_reduce([np.zeros((1, 256), np.uint8)] * 48, [np.ones(1, np.float32)] * 48,
                              np.zeros((1, 48), np.uint32), "bf16")
+
+
+def test_gate_inputs():
+    pins.check_gate_inputs(oracle.gather_rows, oracle.gather_weighted, oracle.gather_reduce)
