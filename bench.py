@@ -144,6 +144,10 @@ def main(argv=None) -> int:
     ap.add_argument("--no-ceiling", action="store_true", help="skip the memory-ceiling probes")
     ap.add_argument("--scale-format", default="f32_row", choices=["f32_row", "e8m0_block32"],
                     help="row scales: one fp32 per row, or 8 E8M0 bytes per row (one per 32 elements)")
+    ap.add_argument("--vocab-map", action="store_true",
+                    help="normalise window ids through a seeded 129,280 -> 99,092 vocabulary map before hashing")
+    ap.add_argument("--prime-rows", action="store_true",
+                    help="per-sub-table prime row counts (the 48 largest primes below the workload's row count)")
     ap.add_argument("--id-batches", type=int, default=1,
                     help="rotate among this many seeded id batches of the same shape (1: the workload's own ids)")
     args = ap.parse_args(argv)
@@ -170,10 +174,17 @@ def main(argv=None) -> int:
         scales = torch.empty((48, w.rows, 8), dtype=torch.uint8, device=dev)
     else:
         scales = torch.empty((48, w.rows), dtype=torch.float32, device=dev)
-    hg.synth_fill(tables, scales, w.table_seed, scale_format=args.scale_format)
+    vocab = workloads.VOCAB if w.ids_kind != "uniform1024" else 1024
+    d_map = torch.from_numpy(workloads.vocab_map(7).view(np.int32)).to(dev) if args.vocab_map else None
+    if args.prime_rows:
+        rows = workloads.prime_rows(48, below=w.rows)
+        tab_list = [tables[s, :rows[s]] for s in range(48)]
+        sc_list = [scales[s, :rows[s]] for s in range(48)]
+    else:
+        tab_list, sc_list = list(tables.unbind(0)), list(scales.unbind(0))
+    hg.synth_fill(tab_list, sc_list, w.table_seed, scale_format=args.scale_format)
     torch.cuda.synchronize()
-    plan = hg.Plan(tables, scales, vocab_size=workloads.VOCAB if w.ids_kind != "uniform1024" else 1024,
-                   scale_format=args.scale_format)
+    plan = hg.Plan(tab_list, sc_list, vocab_size=vocab, scale_format=args.scale_format, vocab_map=d_map)
 
     batches = []
     for b in range(args.id_batches):
@@ -250,7 +261,8 @@ def main(argv=None) -> int:
     else:
         gather_bytes = (GATHER_BYTES_PER_TOKEN - 48 * 4 + scale_bytes) * n_tok
     achieved = gather_bytes / (gather_ms / 1e3) / 1e9
-    traffic = _traffic(n_tok) if args.workload == 4 and not args.dedup and args.id_batches == 1 and not mx else None
+    plain = not (args.dedup or mx or args.vocab_map or args.prime_rows) and args.id_batches == 1
+    traffic = _traffic(n_tok) if args.workload == 4 and plain else None
 
     base = None
     if args.cpu_sample > 0 and args.workload == 4:
@@ -275,6 +287,8 @@ def main(argv=None) -> int:
             "n_tok": n_tok,
             "rows_per_subtable": w.rows,
             "scale_format": args.scale_format,
+            "vocab_map": "seeded 129280 -> 99092" if args.vocab_map else None,
+            "prime_rows": bool(args.prime_rows),
             "id_batches": args.id_batches,
             "step": "engram_hash + engram_dedup + engram_gather_reduce (dedup mode)" if args.dedup
                     else "engram_hash + engram_gather_reduce",

@@ -57,6 +57,7 @@ class PlanDesc(ctypes.Structure):
         ("scales", ctypes.POINTER(ctypes.c_void_p)),
         ("scale_format", ctypes.c_uint32),
         ("reserved1", ctypes.c_uint32),
+        ("vocab_map", ctypes.c_void_p),
     ]
 
 
@@ -134,7 +135,7 @@ class Plan:
     """
 
     def __init__(self, tables, scales, hash_seed: int = DEFAULT_HASH_SEED, vocab_size: int = 0,
-                 scale_format: str = "f32_row"):
+                 scale_format: str = "f32_row", vocab_map: torch.Tensor | None = None):
         if scale_format not in _SCALE_FORMATS:
             raise ValueError(f"scale_format must be one of {sorted(_SCALE_FORMATS)}")
         mx = scale_format == "e8m0_block32"
@@ -157,19 +158,30 @@ class Plan:
             _dev(t, torch.uint8, f"tables[{s}]")
             _dev(c, torch.uint8 if mx else torch.float32, f"scales[{s}]")
             rows.append(t.shape[0])
+        map_ptr = None
+        if vocab_map is not None:
+            if vocab_map.dim() != 1:
+                raise ValueError("vocab_map must be 1-D [vocab_size]")
+            if vocab_size == 0:
+                vocab_size = vocab_map.shape[0]
+            if vocab_map.shape[0] != vocab_size:
+                raise ValueError("vocab_map length must equal vocab_size")
+            map_ptr = _dev(vocab_map, vocab_map.dtype if vocab_map.dtype in (torch.int32, torch.uint32)
+                           else torch.int32, "vocab_map")
         self._build(rows, [t.data_ptr() for t in tables], [c.data_ptr() for c in scales], hash_seed, vocab_size,
-                    keep=(tables, scales), scale_format=_SCALE_FORMATS[scale_format])
+                    keep=(tables, scales, vocab_map), scale_format=_SCALE_FORMATS[scale_format], vocab_map=map_ptr)
 
     @classmethod
     def from_pointers(cls, rows, table_ptrs, scale_ptrs, hash_seed: int = DEFAULT_HASH_SEED, vocab_size: int = 0,
-                      keep=None, scale_format: str = "f32_row") -> "Plan":
+                      keep=None, scale_format: str = "f32_row", vocab_map_ptr: int | None = None) -> "Plan":
         """Plan over raw device pointers (48 each) with the given row counts; ``keep`` is held alive."""
         p = cls.__new__(cls)
         p._build(list(rows), list(table_ptrs), list(scale_ptrs), hash_seed, vocab_size, keep,
-                 scale_format=_SCALE_FORMATS[scale_format])
+                 scale_format=_SCALE_FORMATS[scale_format], vocab_map=vocab_map_ptr)
         return p
 
-    def _build(self, rows, tab_ptrs, sc_ptrs, hash_seed, vocab_size, keep, scale_format: int = SCALE_F32_ROW) -> None:
+    def _build(self, rows, tab_ptrs, sc_ptrs, hash_seed, vocab_size, keep, scale_format: int = SCALE_F32_ROW,
+               vocab_map: int | None = None) -> None:
         if len(rows) != N_SUB or len(tab_ptrs) != N_SUB or len(sc_ptrs) != N_SUB:
             raise ValueError("need 48 row counts, table pointers and scale pointers")
         self._handle = None
@@ -186,6 +198,7 @@ class Plan:
         desc.hash_seed = hash_seed
         desc.vocab_size = vocab_size
         desc.scale_format = scale_format
+        desc.vocab_map = vocab_map
         desc.rows = ctypes.cast(self._rows_c, ctypes.POINTER(ctypes.c_uint64))
         desc.tables = ctypes.cast(self._tabs_c, ctypes.POINTER(ctypes.c_void_p))
         desc.scales = ctypes.cast(self._scs_c, ctypes.POINTER(ctypes.c_void_p))

@@ -60,6 +60,7 @@ int engram_plan(const engram_plan_desc* d, engram_plan_t* out) {
     if (d->scale_format != ENGRAM_SCALE_F32_ROW && d->scale_format != ENGRAM_SCALE_E8M0_BLOCK32)
         return ENGRAM_EUNSUPPORTED;
     if (d->reserved1 != 0) return ENGRAM_EINVAL;
+    if (d->vocab_map && (d->vocab_size == 0 || !aligned(d->vocab_map, 4))) return ENGRAM_EINVAL;
     const uintptr_t scale_align = d->scale_format == ENGRAM_SCALE_F32_ROW ? 4 : 8;
     for (int s = 0; s < kSub; ++s) {
         const uint64_t r = d->rows[s];
@@ -81,6 +82,7 @@ int engram_plan(const engram_plan_desc* d, engram_plan_t* out) {
         p->gather.sc[s] = d->scales[s];
     }
     p->gather.scale_format = d->scale_format;
+    p->hash.vocab_map = d->vocab_map;
     *out = p;
     return ENGRAM_OK;
 }

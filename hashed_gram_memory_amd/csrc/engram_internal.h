@@ -20,7 +20,22 @@ struct HashParams {
     uint64_t mult[kMult];  // M[((m*3 + (n-2))*8 + h)*4 + k]
     uint64_t rows[kSub];   // R_s
     uint64_t magic[kSub];  // floor((2^64 - 1) / R_s): exact x mod R_s with one correction
+    const uint32_t* vocab_map;  // id normalisation applied to window ids, or nullptr
 };
+
+// Window id k of a token: the id k positions back, else the caller's history
+// (history[seq][2] is position -1), else id 0; then the plan's vocabulary map.
+__device__ __forceinline__ uint32_t window_id(const int32_t* __restrict__ ids, const int32_t* __restrict__ history,
+                                              const uint32_t* __restrict__ vocab_map, uint32_t tok, uint32_t seq,
+                                              int32_t t, int k) {
+    int32_t v = 0;
+    if (t - k >= 0)
+        v = ids[tok - k];
+    else if (history)
+        v = history[seq * 3u + static_cast<uint32_t>(3 + t - k)];
+    const uint32_t u = static_cast<uint32_t>(v);
+    return vocab_map ? vocab_map[u] : u;
+}
 
 // Row and scale base pointers of the 48 sub-tables, by value.  sc[s] points
 // at fp32 [R_s] or at uint8 [R_s][8] (E8M0 per 32-element block), as

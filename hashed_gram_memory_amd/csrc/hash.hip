@@ -63,14 +63,7 @@ __global__ __launch_bounds__(384) void hash_kernel(const HashParams P, const int
     // caller's history (history[seq][2] is position -1) or id 0.
     uint64_t w[ENGRAM_MAX_ORDER];
 #pragma unroll
-    for (int k = 0; k < ENGRAM_MAX_ORDER; ++k) {
-        int32_t v = 0;
-        if (t - k >= 0)
-            v = ids[tok - k];
-        else if (history)
-            v = history[seq * 3u + static_cast<uint32_t>(3 + t - k)];
-        w[k] = static_cast<uint32_t>(v);
-    }
+    for (int k = 0; k < ENGRAM_MAX_ORDER; ++k) w[k] = window_id(ids, history, P.vocab_map, tok, seq, t, k);
 
     const uint32_t mbase = wave * (ENGRAM_N_HEADS * ENGRAM_MAX_ORDER);  // multipliers of (m, order, head 0, k 0)
     const uint32_t s0 = m * kRowsPerModule + oi * ENGRAM_N_HEADS;

@@ -49,14 +49,7 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
     const int32_t t = static_cast<int32_t>(tok - seq * seq_len);
     uint64_t w[ENGRAM_MAX_ORDER];
 #pragma unroll
-    for (int k = 0; k < ENGRAM_MAX_ORDER; ++k) {
-        int32_t v = 0;
-        if (t - k >= 0)
-            v = ids[tok - k];
-        else if (history)
-            v = history[seq * 3u + static_cast<uint32_t>(3 + t - k)];
-        w[k] = static_cast<uint32_t>(v);
-    }
+    for (int k = 0; k < ENGRAM_MAX_ORDER; ++k) w[k] = window_id(ids, history, P.h.vocab_map, tok, seq, t, k);
 
     // The module's 24 addresses: q = 8*(order-2) + head.
     const uint32_t s0 = m * kRowsPerModule;

@@ -106,6 +106,15 @@ typedef enum engram_status {
  *       (else ENGRAM_EUNSUPPORTED).
  *   reserved1
  *       Must be 0.
+ *   vocab_map  (device pointer, not copied; NULL = none)
+ *       uint32 [vocab_size]: the id normalisation applied before hashing.
+ *       The pages' engines fold ids that differ only in case, accents or
+ *       spacing into one id of a smaller vocabulary before hashing [GUIDE
+ *       "Engram"]; the map is that table.  Every id of a window (history and
+ *       the pad id 0 included) is replaced by vocab_map[id] before the
+ *       multiply-xor.  Needs vocab_size > 0 (the map's length) and 4-byte
+ *       alignment.  engram_dedup still groups raw windows: equal raw windows
+ *       have equal mapped windows, so its groups stay valid.
  *
  * The plan copies the description; the tables themselves are not copied and
  * must outlive every call that uses the plan.
@@ -123,6 +132,7 @@ typedef struct engram_plan_desc {
     const void* const* scales;
     uint32_t scale_format;
     uint32_t reserved1;            /* must be 0 */
+    const uint32_t* vocab_map;     /* device uint32 [vocab_size] or NULL */
 } engram_plan_desc;
 
 typedef struct engram_plan_s* engram_plan_t;
@@ -152,7 +162,8 @@ int engram_plan_multipliers(engram_plan_t plan, uint64_t* out);
  *
  * Token tok = s*seq_len + t has the id window w_k = id at position t-k,
  * k = 0..3; positions before 0 read history[s][3 + (t-k)] (history[s][2] is
- * the id just before position 0) or, with history == NULL, id 0.  For
+ * the id just before position 0) or, with history == NULL, id 0.  With a
+ * vocab_map in the plan each w_k is then replaced by vocab_map[w_k].  For
  * module m, order n, head h, with u64 the zero-extension of the 32-bit id:
  *     x = XOR_{k<n} ( u64(w_k) * M[m][n][h][k] )   (mod 2^64)
  *     addr[tok][24*m + 8*(n-2) + h] = x mod R_s

@@ -79,13 +79,15 @@ def sub_index(m: int, n: int, h: int) -> int:
 # Step a1: the id window of each token
 # ---------------------------------------------------------------------------
 
-def windows(ids, history=None) -> np.ndarray:
+def windows(ids, history=None, vocab_map=None) -> np.ndarray:
     """Window w[tok] = (w_0, w_1, w_2, w_3), w_k = id at position t - k.
 
     The suffix n-gram of order n ending at a token is (w_{n-1}, ..., w_0)
     [GUIDE "Engram"].  Positions before 0 read history[s][3 + (t - k)] when a
     history is given (history[s][2] is the id just before position 0), else 0.
-    Tokens are numbered sequence-major: tok = s * seq_len + t.
+    Tokens are numbered sequence-major: tok = s * seq_len + t.  With a
+    ``vocab_map`` every window id is then normalised to vocab_map[id], the
+    compressed vocabulary the pages' engines hash [GUIDE "Engram"].
     """
     ids = np.asarray(ids, dtype=np.int64)
     if ids.ndim != 2:
@@ -101,7 +103,10 @@ def windows(ids, history=None) -> np.ndarray:
     w = np.empty((n_seq, seq_len, WINDOW), np.int64)
     for k in range(WINDOW):
         w[:, :, k] = ext[:, WINDOW - 1 - k: WINDOW - 1 - k + seq_len]
-    return w.reshape(n_seq * seq_len, WINDOW)
+    w = w.reshape(n_seq * seq_len, WINDOW)
+    if vocab_map is not None:
+        w = np.asarray(vocab_map, dtype=np.int64)[w]
+    return w
 
 
 # ---------------------------------------------------------------------------
@@ -250,9 +255,10 @@ def gather_weighted(tables, scales, addr, weights, scale_format: str = "f32_row"
     return t.sum(axis=2), np.abs(t).sum(axis=2)
 
 
-def lookup(ids, history, tables, scales, rows, hash_seed: int = DEFAULT_HASH_SEED, scale_format: str = "f32_row"):
+def lookup(ids, history, tables, scales, rows, hash_seed: int = DEFAULT_HASH_SEED, scale_format: str = "f32_row",
+           vocab_map=None):
     """Whole path: windows, hash, gather-reduce.  Returns (addr, out, abs_sum)."""
-    addr = hash_addresses(windows(ids, history), multipliers(hash_seed), rows)
+    addr = hash_addresses(windows(ids, history, vocab_map), multipliers(hash_seed), rows)
     out, abs_sum = gather_reduce(tables, scales, addr, scale_format)
     return addr, out, abs_sum
 

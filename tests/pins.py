@@ -384,3 +384,17 @@ def check_gate_inputs(rows_fn, weighted_fn, gr_fn):
     want = np.einsum("nsj,ns->nsj", rows, w).reshape(N, 2, 24, 256).sum(axis=2)
     assert np.allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
     assert np.all(ab >= np.abs(got) - 1e-9)
+
+
+def check_windows_map(windows_fn):
+    """Every window id -- history and the pad id 0 included -- goes through the map."""
+    vmap = np.arange(20, dtype=np.uint32) + 100
+    vmap[5] = vmap[6] = 9
+    vmap[0] = 7
+    w = windows_fn(np.array([[5, 6, 1]], np.int32), None, vmap)
+    assert np.array_equal(w, [[9, 7, 7, 7], [9, 9, 7, 7], [101, 9, 9, 7]]), w
+    w = windows_fn(np.array([[5]], np.int32), np.array([[2, 3, 6]], np.int32), vmap)
+    assert np.array_equal(w, [[9, 9, 103, 102]]), w
+    ident = np.arange(20, dtype=np.uint32)
+    ids = np.random.default_rng(0).integers(0, 20, size=(3, 9)).astype(np.int32)
+    assert np.array_equal(windows_fn(ids, None, ident), windows_fn(ids, None, None))

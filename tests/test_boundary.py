@@ -266,3 +266,15 @@ def test_gate_io_validation(hg, plan):
     assert L.engram_gather_rows(plan, FAKE, 0, FAKE, None) == OK
     assert L.engram_gather_rows(plan, FAKE, 1, FAKE + 8, None) == EINVAL
     assert L.engram_gather_rows(plan, FAKE, 1 << 31, FAKE, None) == ERANGE
+
+
+def test_plan_vocab_map(hg):
+    d, keep = _desc(hg)
+    d.vocab_map = FAKE
+    assert _plan(hg, d)[0] == EINVAL  # a map needs its length in vocab_size
+    d.vocab_size = 1000
+    st, h = _plan(hg, d)
+    assert st == OK
+    hg.lib().engram_plan_destroy(h)
+    d.vocab_map = FAKE + 2
+    assert _plan(hg, d)[0] == EINVAL

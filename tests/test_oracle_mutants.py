@@ -333,3 +333,28 @@ def _weighted_unweighted(t, s, a, w, fmt="f32_row"):
 ])
 def test_gate_input_mutants_caught(rows_fn, weighted_fn):
     assert _fails(pins.check_gate_inputs, rows_fn, weighted_fn, eo.gather_reduce)
+
+
+def win_map_skips_pad(ids, history=None, vocab_map=None):
+    w = eo.windows(ids, history)
+    if vocab_map is None:
+        return w
+    mapped = np.asarray(vocab_map, np.int64)[w]
+    n_seq, seq_len = np.asarray(ids).shape
+    t = np.tile(np.arange(seq_len), n_seq)
+    for k in range(4):
+        pad = (t - k < 0) & (history is None)
+        mapped[pad, k] = 0
+    return mapped
+
+
+def win_map_before_history(ids, history=None, vocab_map=None):
+    if vocab_map is None:
+        return eo.windows(ids, history)
+    ids = np.asarray(vocab_map, np.int64)[np.asarray(ids)]
+    return eo.windows(ids, history)
+
+
+@pytest.mark.parametrize("mutant", [win_map_skips_pad, win_map_before_history])
+def test_window_map_mutants_caught(mutant):
+    assert _fails(pins.check_windows_map, mutant)

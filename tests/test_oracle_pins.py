@@ -122,3 +122,26 @@ def test_scale_format_rejected():
 
 def test_gate_inputs():
     pins.check_gate_inputs(oracle.gather_rows, oracle.gather_weighted, oracle.gather_reduce)
+
+
+def test_windows_vocab_map():
+    pins.check_windows_map(oracle.windows)
+
+
+def test_vocab_map_merges_rows():
+    """Ids the map folds together hash to the same rows; the others do not."""
+    import workloads
+    vmap = workloads.vocab_map(3, vocab=1000, compressed=600)
+    assert vmap.max() < 600 and len(np.unique(vmap)) == 600
+    a, b = [int(x) for x in np.flatnonzero(vmap == vmap[900])[:2]]
+    ids = np.array([[a, 1, 2], [b, 1, 2]], np.int32)
+    addr = oracle.hash_addresses(oracle.windows(ids, None, vmap), oracle.multipliers(), [1 << 20] * 48)
+    assert np.array_equal(addr[0], addr[3]) and np.array_equal(addr[1], addr[4])
+    raw = oracle.hash_addresses(oracle.windows(ids, None), oracle.multipliers(), [1 << 20] * 48)
+    assert not np.array_equal(raw[0], raw[3])
+
+
+def test_prime_rows():
+    import workloads
+    p = workloads.prime_rows(5, below=100)
+    assert p == [97, 89, 83, 79, 73]

@@ -130,6 +130,43 @@ def uniform_ids(n_seq: int, seq_len: int, seed: int, vocab: int = VOCAB) -> np.n
     return rng.integers(0, vocab, size=(n_seq, seq_len), dtype=np.int64).astype(np.int32)
 
 
+COMPRESSED_VOCAB = 99_092
+
+
+def vocab_map(seed: int = 7, vocab: int = VOCAB, compressed: int = COMPRESSED_VOCAB) -> np.ndarray:
+    """A seeded surjection of ``vocab`` raw ids onto ``compressed`` ids (uint32 [vocab]).
+
+    Stands in for the normalisation table (case, accent and spacing folding
+    into a 99,092-id vocabulary) that needs the real tokenizer: the first
+    ``compressed`` ids map to a random permutation of the compressed range,
+    every further id to a random compressed id, so many raw ids share one.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    m = np.empty(vocab, np.uint32)
+    m[:compressed] = rng.permutation(compressed).astype(np.uint32)
+    m[compressed:] = rng.integers(0, compressed, size=vocab - compressed).astype(np.uint32)
+    return m
+
+
+def prime_rows(count: int = N_SUB, below: int = 1 << 24) -> list[int]:
+    """The ``count`` largest primes below ``below`` (a prime-sized bucket range per sub-table)."""
+    def is_prime(n: int) -> bool:
+        if n < 2 or n % 2 == 0:
+            return n == 2
+        f = 3
+        while f * f <= n:
+            if n % f == 0:
+                return False
+            f += 2
+        return True
+    out, n = [], below - 1
+    while len(out) < count:
+        if is_prime(n):
+            out.append(n)
+        n -= 1
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Table generator (host implementation of the counter-based definition)
 # ---------------------------------------------------------------------------
