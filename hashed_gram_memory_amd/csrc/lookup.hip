@@ -55,17 +55,30 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
     const uint32_t s0 = m * kRowsPerModule;
     const uint32_t mb = m * (kRowsPerModule * ENGRAM_MAX_ORDER);
     uint32_t a[kRowsPerModule];
+    if (POW2) {
+        // Wave-uniform scalar arithmetic; the modulus is a mask.
 #pragma unroll
-    for (int q = 0; q < kRowsPerModule; ++q) {
-        constexpr int kHeads = ENGRAM_N_HEADS;
-        const int order = ENGRAM_MIN_ORDER + q / kHeads;
+        for (int q = 0; q < kRowsPerModule; ++q) {
+            constexpr int kHeads = ENGRAM_N_HEADS;
+            const int order = ENGRAM_MIN_ORDER + q / kHeads;
+            uint64_t x = 0;
+#pragma unroll
+            for (int k = 0; k < order; ++k) x ^= w[k] * P.h.mult[mb + q * ENGRAM_MAX_ORDER + k];
+            a[q] = static_cast<uint32_t>(x & (P.h.rows[s0 + q] - 1u));
+        }
+    } else {
+        // General row counts: lane q < 24 hashes sub-table s0+q in parallel
+        // (exact 64-bit reciprocal modulus), then the 24 results are read
+        // back into wave-uniform registers.
+        const uint32_t q = lane < static_cast<uint32_t>(kRowsPerModule) ? lane : 0u;
+        const uint32_t order = ENGRAM_MIN_ORDER + q / ENGRAM_N_HEADS;
         uint64_t x = 0;
 #pragma unroll
-        for (int k = 0; k < order; ++k) x ^= w[k] * P.h.mult[mb + q * ENGRAM_MAX_ORDER + k];
-        if (POW2)
-            a[q] = static_cast<uint32_t>(x & (P.h.rows[s0 + q] - 1u));
-        else
-            a[q] = mod_rows(x, P.h.rows[s0 + q], P.h.magic[s0 + q]);
+        for (uint32_t k = 0; k < ENGRAM_MAX_ORDER; ++k)
+            if (k < order) x ^= w[k] * P.h.mult[mb + q * ENGRAM_MAX_ORDER + k];
+        const uint32_t mine = mod_rows(x, P.h.rows[s0 + q], P.h.magic[s0 + q]);
+#pragma unroll
+        for (int qq = 0; qq < kRowsPerModule; ++qq) a[qq] = __builtin_amdgcn_readlane(mine, qq);
     }
 
     // All 24 addresses are final before any row or scale is requested: the

@@ -100,3 +100,34 @@ def test_graph_replay_matches_eager():
         assert torch.equal(out_f, eager), rep
         _, want, abs_sum = oracle.lookup(new_ids, new_hist, host_t, host_c, [R] * 48)
         assert_within_tolerance(out.cpu().numpy(), want, abs_sum)
+
+
+def test_launch_chunk_boundary():
+    """More than 2^24 tokens: the gather and the fused lookup split their grids at 2^24 items."""
+    n_tok = (1 << 24) + 37
+    _say(f"chunk boundary, {n_tok} tokens (3.2 GB addresses, 34 GB output)")
+    R = 512
+    host_t, host_c = workloads.dense_tables(808, R)
+    t, c = small_device_tables(host_t, host_c)
+    plan = lib().Plan(t, c)
+    rng = np.random.default_rng(24)
+    ids = rng.integers(0, 129280, size=(1, n_tok), dtype=np.int64).astype(np.int32)
+    d_ids, _ = to_dev_ids(ids, None)
+    addr = lib().hash(plan, d_ids)
+    out = lib().gather_reduce(plan, addr)
+    torch.cuda.synchronize()
+    tokens = np.array([0, 1, 2, 3, (1 << 24) - 2, (1 << 24) - 1, 1 << 24, (1 << 24) + 1, n_tok - 2, n_tok - 1])
+    idx = torch.from_numpy(tokens).cuda()
+    got = out[idx].cpu().numpy()
+    got_addr = addr.view(torch.int32)[idx].cpu().numpy().view(np.uint32)
+    lookup_out = lib().lookup(plan, d_ids, out=out)  # reuse the buffer
+    torch.cuda.synchronize()
+    got_fused = lookup_out[idx].cpu().numpy()
+    del addr, out, lookup_out
+    torch.cuda.empty_cache()
+    win = oracle.windows(ids)[tokens]
+    want_addr = oracle.hash_addresses(win, oracle.multipliers(), [R] * 48)
+    assert np.array_equal(got_addr, want_addr)
+    want, abs_sum = oracle.gather_reduce(host_t, host_c, want_addr)
+    assert_within_tolerance(got, want, abs_sum)
+    assert np.array_equal(got_fused, got)
