@@ -240,6 +240,32 @@ def main(argv=None) -> int:
         del src, dst
 
     ceiling = None if args.no_ceiling or args.dedup else measure_ceiling(hg, torch, plan, tables, addr, out, stream)
+    graph = None
+    if not args.dedup:
+        # the same step captured once into a HIP graph and replayed: the cost without host launch overhead
+        b0 = batches[0]
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            hg.hash(plan, b0[1], b0[2], out=addr)
+            hg.gather_reduce(plan, addr, out=out)
+            hg.lookup(plan, b0[1], b0[2], out=out)
+        stream.wait_stream(side)
+        # 20 steps per graph: one replay shows the device-side time of back-to-back steps
+        per_graph = 20
+        g_two, g_fused = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_two):
+            for _ in range(per_graph):
+                hg.hash(plan, b0[1], b0[2], out=addr)
+                hg.gather_reduce(plan, addr, out=out)
+        with torch.cuda.graph(g_fused):
+            for _ in range(per_graph):
+                hg.lookup(plan, b0[1], b0[2], out=out)
+        reps = 5
+        t_two = _median_ms(torch, g_two.replay, stream, reps) / per_graph
+        t_fused = _median_ms(torch, g_fused.replay, stream, reps) / per_graph
+        graph = {"steps_per_graph": per_graph, "two_call_us_per_step": t_two * 1e3, "fused_us_per_step": t_fused * 1e3}
+        del g_two, g_fused
     fused = None
     if not args.dedup:
         # the same step as one fused launch (engram_lookup): addresses never leave the wave
@@ -309,6 +335,7 @@ def main(argv=None) -> int:
         "hash_gbps": HASH_BYTES_PER_TOKEN * n_tok / (hash_ms / 1e3) / 1e9,
         "gather_bytes_per_launch": gather_bytes,
         "fused_lookup": fused,
+        "graph_replay": graph,
         "ceiling": ceiling,
         "cpu_baseline": base,
     }
