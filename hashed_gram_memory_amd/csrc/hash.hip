@@ -12,9 +12,11 @@
 // lane l of every wave is token l of the block.  A wave's 8 heads share the
 // (module, order), so its 32 multipliers and its 8 (R, magic) pairs are
 // wave-uniform scalar loads from the kernel arguments; the thread reads its
-// token's window (4 ids, cached across the 6 waves) and writes its 8
-// addresses as two 16-byte stores (32 contiguous bytes).  The kernel is
-// store-bound and small next to the gather (196 B per token against ~14.7 KB).
+// token's window (4 ids, cached across the 6 waves) and puts its 8
+// addresses into an LDS tile of the block's 64 x 48 addresses, which the
+// block then writes as one contiguous 12 KiB run with 16-byte stores.  The
+// kernel is store-bound and small next to the gather (196 B per token
+// against ~14.7 KB).
 #include "engram_internal.h"
 
 namespace engram {
@@ -52,8 +54,9 @@ __global__ __launch_bounds__(384) void hash_kernel(const HashParams P, const int
                                                    const int32_t* __restrict__ history, uint32_t n_tok,
                                                    uint32_t seq_len, uint32_t* __restrict__ addr) {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (module, order) = (wave/3, 2+wave%3)
-    const uint32_t tok = blockIdx.x * 64u + (threadIdx.x & 63u);
-    if (tok >= n_tok) return;
+    // Tokens past the end compute a clamped duplicate and are not stored, so
+    // every thread reaches the barrier below.
+    const uint32_t tok = min(blockIdx.x * 64u + (threadIdx.x & 63u), n_tok - 1u);
     const uint32_t m = wave / 3u;
     const uint32_t oi = wave % 3u;  // order - 2
     const uint32_t seq = tok / seq_len;
@@ -74,9 +77,18 @@ __global__ __launch_bounds__(384) void hash_kernel(const HashParams P, const int
         hash_heads<3, POW2>(P, w, mbase, s0, a);
     else
         hash_heads<4, POW2>(P, w, mbase, s0, a);
-    uint4* dst = reinterpret_cast<uint4*>(addr + static_cast<size_t>(tok) * kSub + s0);
-    dst[0] = make_uint4(a[0], a[1], a[2], a[3]);
-    dst[1] = make_uint4(a[4], a[5], a[6], a[7]);
+
+    // Stage the block's 64 x 48 addresses in LDS, then write them out as
+    // one contiguous 12 KiB run with coalesced 16-byte stores.
+    __shared__ uint4 stage[64 * kSub / 4];
+    uint4* my = stage + (threadIdx.x & 63u) * (kSub / 4) + s0 / 4;
+    my[0] = make_uint4(a[0], a[1], a[2], a[3]);
+    my[1] = make_uint4(a[4], a[5], a[6], a[7]);
+    __syncthreads();
+    const uint32_t first = blockIdx.x * 64u;
+    const uint32_t n_vec = (min(64u, n_tok - first) * kSub) / 4u;  // 16-byte words this block owns
+    uint4* dst = reinterpret_cast<uint4*>(addr + static_cast<size_t>(first) * kSub);
+    for (uint32_t i = threadIdx.x; i < n_vec; i += blockDim.x) dst[i] = stage[i];
 }
 
 }  // namespace
