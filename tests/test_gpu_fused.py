@@ -131,3 +131,35 @@ def test_launch_chunk_boundary():
     want, abs_sum = oracle.gather_reduce(host_t, host_c, want_addr)
     assert_within_tolerance(got, want, abs_sum)
     assert np.array_equal(got_fused, got)
+
+
+def test_one_plan_on_two_streams():
+    """A plan is immutable: concurrent calls on two streams give the sequential results."""
+    _say("one plan, two streams")
+    R = 4096
+    host_t, host_c = workloads.dense_tables(10, R)
+    t, c = small_device_tables(host_t, host_c)
+    plan = lib().Plan(t, c, vocab_size=129280)
+    rng = np.random.default_rng(31)
+    batches = [rng.integers(0, 129280, size=(4, 3000)).astype(np.int32) for _ in range(2)]
+    d = [to_dev_ids(b, None)[0] for b in batches]
+    want = [lib().gather_reduce(plan, lib().hash(plan, x)) for x in d]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(want[0]) for _ in range(2)]
+    fused = [torch.empty_like(want[0]) for _ in range(2)]
+    groups_out = [torch.empty_like(want[0]) for _ in range(2)]
+    for rep in range(3):
+        for i, s in enumerate(streams):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                a = lib().hash(plan, d[i], stream=s)
+                lib().gather_reduce(plan, a, out=outs[i], stream=s)
+                lib().lookup(plan, d[i], out=fused[i], stream=s)
+                g = lib().dedup(plan, d[i], stream=s)
+                lib().gather_reduce(plan, a, out=groups_out[i], groups=g, stream=s)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], want[i]), (rep, i)
+            assert torch.equal(fused[i], want[i]), (rep, i)
+            assert torch.equal(groups_out[i], want[i]), (rep, i)
