@@ -57,13 +57,14 @@ def _log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def _traffic(n_tok: int):
-    """HBM bytes per gather launch from the committed counter summary, if it matches the current kernel."""
+def _traffic(n_tok: int, id_batches: int):
+    """HBM bytes per gather launch from the committed counter summary, if it matches the current kernel and run."""
     try:
         rec = json.load(open(PMC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != gather_source_sha256() or rec.get("n_tok") != n_tok:
+    if (rec.get("kernel_source_sha256") != gather_source_sha256() or rec.get("n_tok") != n_tok
+            or rec.get("id_batches") != id_batches):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -148,8 +149,15 @@ def main(argv=None) -> int:
                     help="normalise window ids through a seeded 129,280 -> 99,092 vocabulary map before hashing")
     ap.add_argument("--prime-rows", action="store_true",
                     help="per-sub-table prime row counts (the 48 largest primes below the workload's row count)")
-    ap.add_argument("--id-batches", type=int, default=1,
-                    help="rotate among this many seeded id batches of the same shape (1: the workload's own ids)")
+    ap.add_argument("--uniform-ids", action="store_true",
+                    help="control run: ids uniform over the vocabulary instead of Zipf (no row reuse)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="read this many MiB of scratch before every timed step (evicts L2 and MALL without leaving "
+                         "dirty lines; outside the per-kernel event pairs)")
+    ap.add_argument("--id-batches", type=int, default=4,
+                    help="rotate among this many seeded id batches of the same shape; the first is the workload's own "
+                         "ids.  Rotation keeps a step from reading rows the previous step left in the caches (1: "
+                         "replay the same batch)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -188,7 +196,12 @@ def main(argv=None) -> int:
 
     batches = []
     for b in range(args.id_batches):
-        ids, hist = workloads.make_ids(w, None if b == 0 else w.token_seed + 100 * b)
+        if args.uniform_ids:
+            ids, hist = workloads.uniform_ids(w.n_seq, w.seq_len, w.token_seed + 100 * b), None
+            if w.history:
+                hist = workloads.uniform_ids(w.n_seq, 3, w.token_seed + 100 * b + 1)
+        else:
+            ids, hist = workloads.make_ids(w, None if b == 0 else w.token_seed + 100 * b)
         batches.append((ids, torch.from_numpy(ids).to(dev), None if hist is None else torch.from_numpy(hist).to(dev)))
     addr = torch.empty((n_tok, 48), dtype=torch.uint32, device=dev)
     out = torch.empty((n_tok, 2, 256), dtype=torch.float32, device=dev)
@@ -219,11 +232,15 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    flush = torch.ones(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib > 0 else None
+    flush_sink = torch.zeros((), dtype=torch.uint8, device=dev)
     _log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         e = ev[i]
+        if flush is not None:
+            flush_sink.copy_(flush.max())
         e[0].record(stream)
         hash_phase(i)
         e[1].record(stream)
@@ -255,12 +272,14 @@ def main(argv=None) -> int:
         per_graph = 20
         g_two, g_fused = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_two):
-            for _ in range(per_graph):
-                hg.hash(plan, b0[1], b0[2], out=addr)
+            for j in range(per_graph):
+                b = batches[j % len(batches)]
+                hg.hash(plan, b[1], b[2], out=addr)
                 hg.gather_reduce(plan, addr, out=out)
         with torch.cuda.graph(g_fused):
-            for _ in range(per_graph):
-                hg.lookup(plan, b0[1], b0[2], out=out)
+            for j in range(per_graph):
+                b = batches[j % len(batches)]
+                hg.lookup(plan, b[1], b[2], out=out)
         reps = 5
         t_two = _median_ms(torch, g_two.replay, stream, reps) / per_graph
         t_fused = _median_ms(torch, g_fused.replay, stream, reps) / per_graph
@@ -269,9 +288,14 @@ def main(argv=None) -> int:
     fused = None
     if not args.dedup:
         # the same step as one fused launch (engram_lookup): addresses never leave the wave
-        b0 = batches[0]
-        t_fused = _median_ms(torch, lambda: hg.lookup(plan, b0[1], b0[2], out=out, stream=stream), stream,
-                             max(5, min(args.steps, 50)))
+        turn = [0]
+
+        def fused_step():
+            b = batches[turn[0] % len(batches)]
+            turn[0] += 1
+            hg.lookup(plan, b[1], b[2], out=out, stream=stream)
+
+        t_fused = _median_ms(torch, fused_step, stream, max(5, min(args.steps, 50)))
         fused = {"us_per_step": t_fused * 1e3, "tokens_per_s": n_tok / (t_fused / 1e3)}
 
     hash_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
@@ -287,8 +311,8 @@ def main(argv=None) -> int:
     else:
         gather_bytes = (GATHER_BYTES_PER_TOKEN - 48 * 4 + scale_bytes) * n_tok
     achieved = gather_bytes / (gather_ms / 1e3) / 1e9
-    plain = not (args.dedup or mx or args.vocab_map or args.prime_rows) and args.id_batches == 1
-    traffic = _traffic(n_tok) if args.workload == 4 and plain else None
+    plain = not (args.dedup or mx or args.vocab_map or args.prime_rows or args.uniform_ids or args.flush_mib)
+    traffic = _traffic(n_tok, args.id_batches) if args.workload == 4 and plain else None
 
     base = None
     if args.cpu_sample > 0 and args.workload == 4:
@@ -315,6 +339,8 @@ def main(argv=None) -> int:
             "scale_format": args.scale_format,
             "vocab_map": "seeded 129280 -> 99092" if args.vocab_map else None,
             "prime_rows": bool(args.prime_rows),
+            "ids": "uniform over 129280 (control)" if args.uniform_ids else "Zipf(1.1) over 129280",
+            "flush_mib_per_step": args.flush_mib,
             "id_batches": args.id_batches,
             "step": "engram_hash + engram_dedup + engram_gather_reduce (dedup mode)" if args.dedup
                     else "engram_hash + engram_gather_reduce",
