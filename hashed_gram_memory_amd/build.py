@@ -17,6 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libengram.so")
+DEMO_SRC = os.path.join(CSRC, "examples", "c_abi_demo.c")
+DEMO = os.path.join(HERE, "c_abi_demo")
 SOURCES = ["engram_api.cpp", "hash.hip", "gather_reduce.hip", "dedup.hip", "synth_fill.hip", "probe.hip", "lookup.hip", "gate_io.hip"]
 ARCH = "gfx950"
 
@@ -55,8 +57,16 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # A plain C consumer of the ABI (host code only), linked against the library just built.
+    cmd = ["gcc", "-O2", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I", "/opt/rocm/include", DEMO_SRC,
+           "-o", DEMO + ".tmp", "-L", HERE, "-lengram", "-L", "/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"c_abi_demo build failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(DEMO + ".tmp", DEMO)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", DEMO)
     return LIB
 
 
