@@ -123,9 +123,15 @@ def measure_ceiling(hg, torch, plan, tables, addr, out, stream):
     n_tok = addr.shape[0]
     t_rows = _median_ms(torch, lambda: hg.probe_rows(plan, addr, out, stream=stream), stream, 10)
     rows_bytes = n_tok * (48 * 256 + 48 * 4 + 2 * 256 * 4)
+    rand = {}
+    random_bytes = 2 << 30
+    for chunk in (256, 512, 1024):
+        t = _median_ms(torch, lambda: hg.probe_random(flat, chunk, random_bytes, sink, stream=stream), stream, 5)
+        rand[f"random_{chunk}B_read_GBps"] = random_bytes / (t / 1e3) / 1e9
     return {
         "stream_read_GBps": read_bytes / (t_read / 1e3) / 1e9,
         "stream_copy_GBps": 2 * copy_bytes / (t_copy / 1e3) / 1e9,
+        **rand,
         "gather_rows_only_us": t_rows * 1e3,
         "gather_rows_only_GBps": rows_bytes / (t_rows / 1e3) / 1e9,
     }

@@ -83,6 +83,7 @@ def _load():
         "engram_probe_read": [VP, U64, VP, VP],
         "engram_probe_copy": [VP, VP, U64, VP],
         "engram_probe_rows": [P, VP, I64, VP, VP],
+        "engram_probe_random": [VP, U64, U32, U64, U64, VP, VP],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -408,6 +409,15 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
         raise ValueError("src and dst must be device tensors of the same byte size")
     _check(_lib.engram_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes - nbytes % 16, _stream(stream)),
            "engram_probe_copy")
+
+
+def probe_random(buf: torch.Tensor, chunk_bytes: int, read_bytes: int, sink: torch.Tensor, seed: int = 1,
+                 stream=None) -> None:
+    """Random reads of whole ``chunk_bytes`` chunks of the contiguous device tensor ``buf`` (engram_probe_random)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _check(_lib.engram_probe_random(buf.data_ptr(), buf.numel() * buf.element_size(), chunk_bytes, read_bytes, seed,
+                                    _dev(sink, torch.int32, "sink"), _stream(stream)), "engram_probe_random")
 
 
 def probe_rows(plan: Plan, addr: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:

@@ -9,14 +9,52 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Streaming read: 4 independent 16-byte non-temporal loads per thread per
+// iteration, so enough bytes are in flight to reach the DRAM ceiling.
 __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, uint64_t n, uint32_t* sink) {
     uint32_t x = 0;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
-    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n; i += stride) {
         const u32x4 v = __builtin_nontemporal_load(src + i);
         x ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     if (x == 0x9E3779B9u) *sink = x;  // keeps the loads; practically never taken
+}
+
+__device__ __forceinline__ uint64_t probe_mix(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Random reads of whole CHUNK-byte blocks: each wave reads K chunks at
+// uniformly random chunk-aligned offsets (64 lanes x 4 B per 256 bytes).
+template <int CHUNK, int K>
+__global__ __launch_bounds__(256) void random_kernel(const uint32_t* __restrict__ buf, uint64_t n_chunks, uint64_t seed,
+                                                     uint32_t* sink) {
+    constexpr int kLoads = CHUNK / 256;
+    const uint64_t wave = static_cast<uint64_t>(blockIdx.x) * 4u + (threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63u;
+    uint32_t v[K * kLoads];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const uint64_t r = __umul64hi(probe_mix(seed + wave * K + k), n_chunks);
+        const uint32_t* p = buf + r * (CHUNK / 4);
+#pragma unroll
+        for (int c = 0; c < kLoads; ++c) v[k * kLoads + c] = __builtin_nontemporal_load(p + c * 64 + lane);
+    }
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < K * kLoads; ++i) x ^= v[i];
+    if (x == 0x9E3779B9u) *sink = x;
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n) {
@@ -68,8 +106,30 @@ using namespace engram;
 extern "C" int engram_probe_read(const void* src, uint64_t bytes, uint32_t* sink, void* stream) {
     if (!src || !sink || bytes % 16 || !aligned(src, 16) || !aligned(sink, 4)) return ENGRAM_EINVAL;
     if (bytes == 0) return ENGRAM_OK;
-    hipLaunchKernelGGL(read_kernel, dim3(8192), dim3(256), 0, static_cast<hipStream_t>(stream),
+    hipLaunchKernelGGL(read_kernel, dim3(16384), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4*>(src), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
+}
+
+extern "C" int engram_probe_random(const void* buf, uint64_t bytes, uint32_t chunk_bytes, uint64_t read_bytes,
+                                   uint64_t seed, uint32_t* sink, void* stream) {
+    if (!buf || !sink || !aligned(buf, 256) || !aligned(sink, 4)) return ENGRAM_EINVAL;
+    if (chunk_bytes != 256 && chunk_bytes != 512 && chunk_bytes != 1024) return ENGRAM_EUNSUPPORTED;
+    const uint64_t n_chunks = bytes / chunk_bytes;
+    if (n_chunks == 0) return ENGRAM_EINVAL;
+    // 24 chunks of 256 B or 12 of 512 B or 6 of 1 KiB per wave: 6 KiB per wave, as the gather's (token, module).
+    const uint64_t waves = read_bytes / 6144u;
+    if (waves == 0) return ENGRAM_OK;
+    if (waves / 4u > 0x7FFFFFFFu) return ENGRAM_ERANGE;
+    const dim3 grid(static_cast<uint32_t>((waves + 3u) / 4u)), block(256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint32_t* b = static_cast<const uint32_t*>(buf);
+    if (chunk_bytes == 256)
+        hipLaunchKernelGGL((random_kernel<256, 24>), grid, block, 0, s, b, n_chunks, seed, sink);
+    else if (chunk_bytes == 512)
+        hipLaunchKernelGGL((random_kernel<512, 12>), grid, block, 0, s, b, n_chunks, seed, sink);
+    else
+        hipLaunchKernelGGL((random_kernel<1024, 6>), grid, block, 0, s, b, n_chunks, seed, sink);
     return hipGetLastError() == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
 }
 

@@ -11,6 +11,8 @@
  *     wave layout and row loads as engram_gather_reduce, decoded rows summed
  *     without scaling, so its cost minus the full kernel's is the cost of the
  *     48 random 4-byte scale reads.
+ *   - random reads of whole 256-, 512- or 1024-byte chunks: how efficiently
+ *     DRAM serves accesses of the gather's size (a row is 256 bytes).
  * All return 0 or a negative engram_status; all are asynchronous on
  * `stream` and allocate nothing.
  */
@@ -33,6 +35,14 @@ int engram_probe_read(const void* src, uint64_t bytes, uint32_t* sink, void* str
 /* Copy `bytes` (a multiple of 16) from `src` to `dst` (both 16-byte aligned,
  * not overlapping). */
 int engram_probe_copy(const void* src, void* dst, uint64_t bytes, void* stream);
+
+/* Read about `read_bytes` in whole `chunk_bytes` chunks (256, 512 or 1024,
+ * else ENGRAM_EUNSUPPORTED) at uniformly random chunk offsets of the device
+ * buffer `buf` (`bytes` long, 256-byte aligned), 6 KiB per wavefront; offsets
+ * come from splitmix64 of (seed, chunk counter).  `sink` as for
+ * engram_probe_read. */
+int engram_probe_random(const void* buf, uint64_t bytes, uint32_t chunk_bytes, uint64_t read_bytes, uint64_t seed,
+                        uint32_t* sink, void* stream);
 
 /* engram_gather_reduce in direct mode without the row scales: out[tok][m][j]
  * = sum over the module's 24 rows of the decoded code.  Same arguments and

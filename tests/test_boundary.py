@@ -278,3 +278,12 @@ def test_plan_vocab_map(hg):
     hg.lib().engram_plan_destroy(h)
     d.vocab_map = FAKE + 2
     assert _plan(hg, d)[0] == EINVAL
+
+
+def test_probe_random_validation(hg):
+    L = hg.lib()
+    assert L.engram_probe_random(None, 1 << 20, 256, 1 << 20, 1, FAKE, None) == EINVAL
+    assert L.engram_probe_random(FAKE + 16, 1 << 20, 256, 1 << 20, 1, FAKE, None) == EINVAL
+    assert L.engram_probe_random(FAKE, 1 << 20, 300, 1 << 20, 1, FAKE, None) == EUNSUPPORTED
+    assert L.engram_probe_random(FAKE, 100, 256, 1 << 20, 1, FAKE, None) == EINVAL
+    assert L.engram_probe_random(FAKE, 1 << 20, 256, 100, 1, FAKE, None) == OK  # less than one wave: nothing to do
