@@ -128,10 +128,16 @@ def measure_ceiling(hg, torch, plan, tables, addr, out, stream):
     for chunk in (256, 512, 1024):
         t = _median_ms(torch, lambda: hg.probe_random(flat, chunk, random_bytes, sink, stream=stream), stream, 5)
         rand[f"random_{chunk}B_read_GBps"] = random_bytes / (t / 1e3) / 1e9
+    # the same random-row gather-sum with the row scales in four places: what DRAM charges per row
+    layouts = {}
+    for name in hg.PROBE_RECORD_LAYOUTS:
+        t = _median_ms(torch, lambda: hg.probe_records(flat, name, out, stream=stream), stream, 5)
+        layouts[name] = t * 1e3
     return {
         "stream_read_GBps": read_bytes / (t_read / 1e3) / 1e9,
         "stream_copy_GBps": 2 * copy_bytes / (t_copy / 1e3) / 1e9,
         **rand,
+        "random_rows_us": layouts,
         "gather_rows_only_us": t_rows * 1e3,
         "gather_rows_only_GBps": rows_bytes / (t_rows / 1e3) / 1e9,
     }
@@ -304,6 +310,13 @@ def main(argv=None) -> int:
         t_fused = _median_ms(torch, fused_step, stream, max(5, min(args.steps, 50)))
         fused = {"us_per_step": t_fused * 1e3, "tokens_per_s": n_tok / (t_fused / 1e3)}
 
+    # distinct (sub-table, row) pairs of the first batch: the bytes a perfect cache would still fetch
+    b0 = batches[0]
+    hg.hash(plan, b0[1], b0[2], out=addr, stream=stream)
+    keys = addr.view(torch.int32).cpu().numpy().view(np.uint32).astype(np.uint64)
+    keys |= np.arange(48, dtype=np.uint64)[None, :] << np.uint64(32)
+    distinct = int(np.unique(keys).size)
+
     hash_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     gather_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_per_step = wall / args.steps * 1e3
@@ -366,6 +379,11 @@ def main(argv=None) -> int:
         "us_per_step": ms_per_step * 1e3,
         "hash_gbps": HASH_BYTES_PER_TOKEN * n_tok / (hash_ms / 1e3) / 1e9,
         "gather_bytes_per_launch": gather_bytes,
+        "unique_rows": {
+            "distinct_rows": distinct,
+            "row_reads": 48 * n_tok,
+            "bytes": distinct * (256 + scale_bytes // 48) + n_tok * 2 * 256 * 4,
+        },
         "fused_lookup": fused,
         "graph_replay": graph,
         "ceiling": ceiling,

@@ -84,6 +84,7 @@ def _load():
         "engram_probe_copy": [VP, VP, U64, VP],
         "engram_probe_rows": [P, VP, I64, VP, VP],
         "engram_probe_random": [VP, U64, U32, U64, U64, VP, VP],
+        "engram_probe_records": [VP, U64, U32, I64, U64, VP, VP],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -418,6 +419,21 @@ def probe_random(buf: torch.Tensor, chunk_bytes: int, read_bytes: int, sink: tor
         raise ValueError("buf must be a contiguous device tensor")
     _check(_lib.engram_probe_random(buf.data_ptr(), buf.numel() * buf.element_size(), chunk_bytes, read_bytes, seed,
                                     _dev(sink, torch.int32, "sink"), _stream(stream)), "engram_probe_random")
+
+
+PROBE_RECORD_LAYOUTS = ("rows_only", "separate_f32", "inline_f32_260", "inline_e8m0_264")
+
+
+def probe_records(buf: torch.Tensor, layout: str, out: torch.Tensor, seed: int = 1, stream=None) -> None:
+    """Random-row gather-sum with the row scales placed per ``layout`` (engram_probe_records); ``out`` is fp32
+    [n_tok, 2, 256] and sets the token count."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if out.dtype != torch.float32 or out.dim() != 3 or tuple(out.shape[1:]) != (2, 256) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [n_tok, 2, 256] tensor")
+    _check(_lib.engram_probe_records(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                     PROBE_RECORD_LAYOUTS.index(layout), out.shape[0], seed, out.data_ptr(),
+                                     _stream(stream)), "engram_probe_records")
 
 
 def probe_rows(plan: Plan, addr: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:

@@ -29,16 +29,12 @@ __global__ __launch_bounds__(256) void gather_weighted_kernel(const GatherParams
     const uint32_t tok = tok_base + group * 4u + wave;
     if (tok >= n_tok) return;
     const uint32_t s0 = module * kRowsPerModule;
-    const uint32_t* ta = addr + static_cast<size_t>(tok) * kSub + s0;
-    const float* tw = weights + static_cast<size_t>(tok) * kSub + s0;
-    uint32_t a[kRowsPerModule];
-    float w[kRowsPerModule];
-#pragma unroll
-    for (int q = 0; q < kRowsPerModule; ++q) {
-        a[q] = ta[q];
-        w[q] = tw[q];
-    }
-    const f32x4 acc = weighted_sum_rows<FMT>(P, s0, a, w, lane);
+    const size_t own = static_cast<size_t>(tok) * kSub + s0 + owned_row(lane);
+    const uint32_t a = addr[own];
+    const float w = weights[own];
+    RowSet r;
+    load_rows<FMT>(P, s0, a, lane, r);
+    const f32x4 acc = weighted_sum_rows<FMT>(r, w, lane);
     __builtin_nontemporal_store(
         acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + module * kRowBytes + lane * 4u));
 }
@@ -55,17 +51,14 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const GatherParams P, 
     const uint32_t tok = tok_base + group * 4u + wave;
     if (tok >= n_tok) return;
     const uint32_t s0 = module * kRowsPerModule;
-    const uint32_t* ta = addr + static_cast<size_t>(tok) * kSub + s0;
-    uint32_t a[kRowsPerModule];
-#pragma unroll
-    for (int q = 0; q < kRowsPerModule; ++q) a[q] = ta[q];
-    uint32_t v[kRowsPerModule];
-    float sc[kRowsPerModule];
-    load_rows<FMT, false>(P, s0, a, lane, v, sc);
+    const uint32_t a = addr[static_cast<size_t>(tok) * kSub + s0 + owned_row(lane)];
+    RowSet r;
+    load_rows<FMT>(P, s0, a, lane, r);
     float* dst = rows + (static_cast<size_t>(tok) * kSub + s0) * kRowBytes + lane * 4u;
 #pragma unroll
-    for (int q = 0; q < kRowsPerModule; ++q)
-        __builtin_nontemporal_store(decode_word(v[q], sc[q]), reinterpret_cast<f32x4*>(dst + q * kRowBytes));
+    for (int k = 0; k < kRowsPerModule; ++k)
+        __builtin_nontemporal_store(decode_word(r.v[k], row_scale<FMT>(r, k, lane)),
+                                    reinterpret_cast<f32x4*>(dst + k * kRowBytes));
 }
 
 template <int FMT>

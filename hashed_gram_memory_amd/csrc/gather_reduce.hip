@@ -13,9 +13,11 @@
 // Mapping (gfx950, wave64):
 //   * one wavefront per (token, module); a row is one coalesced
 //     global_load_dword of 64 lanes x 4 B, lane l holding elements 4l..4l+3;
-//   * the 24 addresses of a (token, module) are contiguous and wave-uniform
-//     (scalar loads), as are the 24 row bases and the 24 scales (or, with
-//     block scales, the 24 rows' 8-byte scale groups);
+//   * the 24 addresses of a (token, module) are contiguous: lane q < 24 loads
+//     address q, forms row q's base and loads row q's scale (or its 8-byte
+//     group of block scales), so the addresses and the 24 scales each take
+//     one vector load; row bases are broadcast from their lane one at a time
+//     (few scalar registers live: 8 waves per SIMD fit);
 //   * all 24 row loads are issued before the first is consumed, so a wave
 //     keeps 24 x 256 B in flight; with up to 8 waves per SIMD that is
 //     ~200 KB in flight per CU;
@@ -58,21 +60,26 @@ __global__ __launch_bounds__(256) void gather_reduce_kernel(const GatherParams P
     uint32_t tok = item;
     if (kDedup) tok = static_cast<uint32_t>(perm[offsets[item]]);
     const uint32_t s0 = module * kRowsPerModule;
-    const uint32_t* ta = addr + static_cast<size_t>(tok) * kSub + s0;  // the module's 24 addresses
-    uint32_t a[kRowsPerModule];
-#pragma unroll
-    for (int q = 0; q < kRowsPerModule; ++q) a[q] = ta[q];
-    const f32x4 acc = sum_rows<FMT>(P, s0, a, lane);
+    // lane q < 24 takes the address of the module's row q (one coalesced load)
+    const uint32_t a = addr[static_cast<size_t>(tok) * kSub + s0 + owned_row(lane)];
+    RowSet r;
+    load_rows<FMT>(P, s0, a, lane, r);
+    const f32x4 acc = sum_rows<FMT>(r, lane);
 
     const size_t col = static_cast<size_t>(module) * kRowBytes + lane * 4u;
     if (!kDedup) {
         __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + col));
     } else {
+        // A group has at least one member (the token read above), so the
+        // first store is unconditional; a loop that could run zero times
+        // would let the compiler sink the loads below a branch that the
+        // row-base broadcasts cannot follow, keeping all 24 live at once.
+        int32_t i = offsets[item];
         const int32_t end = offsets[item + 1];
-        for (int32_t i = offsets[item]; i < end; ++i) {
+        do {
             const uint32_t t = static_cast<uint32_t>(perm[i]);
             __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(t) * (2 * kRowBytes) + col));
-        }
+        } while (++i < end);
     }
 }
 

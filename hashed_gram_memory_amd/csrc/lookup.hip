@@ -9,11 +9,13 @@
 // which is what a decode step of a few tokens is made of.
 //
 // Mapping: as gather_reduce_kernel (one wave per (token, module), XCDs 0-3
-// module 0, XCDs 4-7 module 1).  The window ids, the multipliers and the 24
-// addresses are wave-uniform (scalar registers); the hash is the same
-// multiply-xor and modulus as hash_kernel, and the accumulation the same
-// fused multiply-add sequence as gather_reduce_kernel, so the result is
-// bitwise identical to engram_hash followed by engram_gather_reduce.
+// module 0, XCDs 4-7 module 1).  The window ids are wave-uniform; lane q < 24
+// hashes row q of the module in parallel with the others, with the same
+// multiply-xor and modulus (a mask for power-of-two row counts) as
+// hash_kernel, and then owns that row in the lane-addressed loads.  The
+// accumulation is the fused multiply-add sequence of gather_reduce_kernel, so
+// the result is bitwise identical to engram_hash followed by
+// engram_gather_reduce.
 #include "row_sum.h"
 
 namespace engram {
@@ -51,41 +53,22 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
 #pragma unroll
     for (int k = 0; k < ENGRAM_MAX_ORDER; ++k) w[k] = window_id(ids, history, P.h.vocab_map, tok, seq, t, k);
 
-    // The module's 24 addresses: q = 8*(order-2) + head.
+    // Lane q < 24 hashes the module's row q = 8*(order-2) + head (lanes
+    // 24..63 repeat row 0) and keeps the address for the lane-addressed loads.
     const uint32_t s0 = m * kRowsPerModule;
     const uint32_t mb = m * (kRowsPerModule * ENGRAM_MAX_ORDER);
-    uint32_t a[kRowsPerModule];
-    if (POW2) {
-        // Wave-uniform scalar arithmetic; the modulus is a mask.
+    const uint32_t q = owned_row(lane);
+    const uint32_t order = ENGRAM_MIN_ORDER + q / ENGRAM_N_HEADS;
+    uint64_t x = 0;
 #pragma unroll
-        for (int q = 0; q < kRowsPerModule; ++q) {
-            constexpr int kHeads = ENGRAM_N_HEADS;
-            const int order = ENGRAM_MIN_ORDER + q / kHeads;
-            uint64_t x = 0;
-#pragma unroll
-            for (int k = 0; k < order; ++k) x ^= w[k] * P.h.mult[mb + q * ENGRAM_MAX_ORDER + k];
-            a[q] = static_cast<uint32_t>(x & (P.h.rows[s0 + q] - 1u));
-        }
-    } else {
-        // General row counts: lane q < 24 hashes sub-table s0+q in parallel
-        // (exact 64-bit reciprocal modulus), then the 24 results are read
-        // back into wave-uniform registers.
-        const uint32_t q = lane < static_cast<uint32_t>(kRowsPerModule) ? lane : 0u;
-        const uint32_t order = ENGRAM_MIN_ORDER + q / ENGRAM_N_HEADS;
-        uint64_t x = 0;
-#pragma unroll
-        for (uint32_t k = 0; k < ENGRAM_MAX_ORDER; ++k)
-            if (k < order) x ^= w[k] * P.h.mult[mb + q * ENGRAM_MAX_ORDER + k];
-        const uint32_t mine = mod_rows(x, P.h.rows[s0 + q], P.h.magic[s0 + q]);
-#pragma unroll
-        for (int qq = 0; qq < kRowsPerModule; ++qq) a[qq] = __builtin_amdgcn_readlane(mine, qq);
-    }
+    for (uint32_t k = 0; k < ENGRAM_MAX_ORDER; ++k)
+        if (k < order) x ^= w[k] * P.h.mult[mb + q * ENGRAM_MAX_ORDER + k];
+    const uint64_t R = P.h.rows[s0 + q];
+    const uint32_t a = POW2 ? static_cast<uint32_t>(x & (R - 1u)) : mod_rows(x, R, P.h.magic[s0 + q]);
 
-    // All 24 addresses are final before any row or scale is requested: the
-    // multipliers are scalar loads too, and a scalar-load wait would
-    // otherwise also wait for the (HBM-latency) scale loads issued so far.
-    __builtin_amdgcn_sched_barrier(0);
-    const f32x4 acc = sum_rows<FMT, true>(P.g, s0, a, lane);
+    RowSet r;
+    load_rows<FMT>(P.g, s0, a, lane, r);
+    const f32x4 acc = sum_rows<FMT>(r, lane);
     __builtin_nontemporal_store(
         acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + m * kRowBytes + lane * 4u));
 }

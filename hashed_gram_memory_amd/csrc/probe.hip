@@ -1,5 +1,7 @@
 // Memory-ceiling probes (measurement only): streaming read, streaming copy,
-// and the gather without its scale reads.  See engram_probe.h.
+// random whole-chunk reads, random-row gathers with the row scales in
+// different places, and the gather without its scale reads.  See
+// engram_probe.h.
 #include "engram_internal.h"
 #include "engram_probe.h"
 
@@ -55,6 +57,54 @@ __global__ __launch_bounds__(256) void random_kernel(const uint32_t* __restrict_
 #pragma unroll
     for (int i = 0; i < K * kLoads; ++i) x ^= v[i];
     if (x == 0x9E3779B9u) *sink = x;
+}
+
+// Random-row gather-sum with the row scales in one of four places, to measure
+// what DRAM charges for them (one wave per (token, module), 24 random rows):
+//   0  256-byte rows, no scales (two 128-byte lines per row)
+//   1  256-byte rows, fp32 scales in a separate array after the rows
+//   2  260-byte records: codes, then the fp32 scale
+//   3  264-byte records: codes, then 8 E8M0 block exponents
+template <int LAYOUT>
+__global__ __launch_bounds__(256) void records_kernel(const uint8_t* __restrict__ buf, uint64_t n_rec,
+                                                      uint64_t n_waves, uint64_t seed, float* __restrict__ out) {
+    constexpr uint64_t kStride = LAYOUT <= 1 ? 256 : (LAYOUT == 2 ? 260 : 264);
+    const uint64_t wave = static_cast<uint64_t>(blockIdx.x) * 4u + (threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63u;
+    if (wave >= n_waves) return;
+    // lane q < 24 draws row q's index; the wave reads them back one by one
+    const uint64_t r_lane = __umul64hi(probe_mix(seed + wave * 24u + lane % 24u), n_rec);
+    const uint32_t r_lo = static_cast<uint32_t>(r_lane), r_hi = static_cast<uint32_t>(r_lane >> 32);
+    const float* sep = reinterpret_cast<const float*>(buf + n_rec * 256u);
+    uint32_t v[24], e8[24];
+    float sc[24];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 24; ++q) {
+        const uint64_t r = __builtin_amdgcn_readlane(r_lo, q) |
+                           (static_cast<uint64_t>(__builtin_amdgcn_readlane(r_hi, q)) << 32);
+        const uint8_t* rec = buf + r * kStride;
+        v[q] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(rec) + lane);
+        if (LAYOUT == 1) sc[q] = sep[r];
+        if (LAYOUT == 2) sc[q] = *reinterpret_cast<const float*>(rec + 256);
+        if (LAYOUT == 3) e8[q] = rec[256 + (lane >> 3)];
+        if (LAYOUT == 0) sc[q] = 1.0f;
+    }
+    if (LAYOUT == 3) {
+#pragma unroll
+        for (int q = 0; q < 24; ++q) sc[q] = __builtin_bit_cast(float, ((e8[q] & 0x7Fu) + 64u) << 23);  // finite
+    }
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < 24; ++q) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[q]), false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v[q]), true);
+        acc.x = __builtin_fmaf(lo[0], sc[q], acc.x);
+        acc.y = __builtin_fmaf(lo[1], sc[q], acc.y);
+        acc.z = __builtin_fmaf(hi[0], sc[q], acc.z);
+        acc.w = __builtin_fmaf(hi[1], sc[q], acc.w);
+    }
+    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + wave * 256u) + lane);
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, uint64_t n) {
@@ -158,4 +208,26 @@ extern "C" int engram_probe_rows(engram_plan_t p, const uint32_t* addr, int64_t 
         if (hipGetLastError() != hipSuccess) return ENGRAM_EHIP;
     }
     return ENGRAM_OK;
+}
+
+extern "C" int engram_probe_records(const void* buf, uint64_t bytes, uint32_t layout, int64_t n_tok, uint64_t seed,
+                                    float* out, void* stream) {
+    if (!buf || !out || !aligned(buf, 256) || !aligned(out, 16) || n_tok < 0) return ENGRAM_EINVAL;
+    if (layout > 3) return ENGRAM_EUNSUPPORTED;
+    const uint64_t stride = layout == 0 ? 256u : (layout == 3 ? 264u : 260u);  // layout 1: 256 B row + 4 B scale
+    const uint64_t n_rec = bytes / stride;
+    if (n_rec == 0) return ENGRAM_EINVAL;
+    if (n_tok == 0) return ENGRAM_OK;
+    const uint64_t n_waves = 2u * static_cast<uint64_t>(n_tok);
+    if ((n_waves + 3u) / 4u > 0x7FFFFFFFu) return ENGRAM_ERANGE;
+    const dim3 grid(static_cast<uint32_t>((n_waves + 3u) / 4u)), block(256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t* b = static_cast<const uint8_t*>(buf);
+    switch (layout) {
+        case 0: hipLaunchKernelGGL(records_kernel<0>, grid, block, 0, s, b, n_rec, n_waves, seed, out); break;
+        case 1: hipLaunchKernelGGL(records_kernel<1>, grid, block, 0, s, b, n_rec, n_waves, seed, out); break;
+        case 2: hipLaunchKernelGGL(records_kernel<2>, grid, block, 0, s, b, n_rec, n_waves, seed, out); break;
+        default: hipLaunchKernelGGL(records_kernel<3>, grid, block, 0, s, b, n_rec, n_waves, seed, out); break;
+    }
+    return hipGetLastError() == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
 }

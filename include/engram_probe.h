@@ -12,7 +12,9 @@
  *     without scaling, so its cost minus the full kernel's is the cost of the
  *     48 random 4-byte scale reads.
  *   - random reads of whole 256-, 512- or 1024-byte chunks: how efficiently
- *     DRAM serves accesses of the gather's size (a row is 256 bytes).
+ *     DRAM serves accesses of the gather's size (a row is 256 bytes);
+ *   - a random-row gather-sum with the row scales kept in different places:
+ *     what DRAM charges for the scale of a row.
  * All return 0 or a negative engram_status; all are asynchronous on
  * `stream` and allocate nothing.
  */
@@ -43,6 +45,19 @@ int engram_probe_copy(const void* src, void* dst, uint64_t bytes, void* stream);
  * engram_probe_read. */
 int engram_probe_random(const void* buf, uint64_t bytes, uint32_t chunk_bytes, uint64_t read_bytes, uint64_t seed,
                         uint32_t* sink, void* stream);
+
+/* Gather-sum of 24 uniformly random rows per (token, module) of the device
+ * buffer `buf` (`bytes` long, 256-byte aligned), writing fp32 [n_tok][2][256]
+ * to `out` (16-byte aligned).  `layout` places the row scales:
+ *   0  256-byte rows, no scales           (rows: bytes / 256)
+ *   1  256-byte rows + fp32 scales in a separate array after all the rows
+ *                                         (rows: bytes / 260)
+ *   2  260-byte records, fp32 scale after the 256 codes (rows: bytes / 260)
+ *   3  264-byte records, 8 E8M0 bytes after the codes   (rows: bytes / 264)
+ * Any other layout is ENGRAM_EUNSUPPORTED.  The buffer's contents only need
+ * to be readable; the output is for keeping the loads, not for checking. */
+int engram_probe_records(const void* buf, uint64_t bytes, uint32_t layout, int64_t n_tok, uint64_t seed, float* out,
+                         void* stream);
 
 /* engram_gather_reduce in direct mode without the row scales: out[tok][m][j]
  * = sum over the module's 24 rows of the decoded code.  Same arguments and

@@ -287,3 +287,14 @@ def test_probe_random_validation(hg):
     assert L.engram_probe_random(FAKE, 1 << 20, 300, 1 << 20, 1, FAKE, None) == EUNSUPPORTED
     assert L.engram_probe_random(FAKE, 100, 256, 1 << 20, 1, FAKE, None) == EINVAL
     assert L.engram_probe_random(FAKE, 1 << 20, 256, 100, 1, FAKE, None) == OK  # less than one wave: nothing to do
+
+
+def test_probe_records_validation(hg):
+    L = hg.lib()
+    assert L.engram_probe_records(None, 1 << 20, 0, 4, 1, FAKE, None) == EINVAL
+    assert L.engram_probe_records(FAKE + 16, 1 << 20, 0, 4, 1, FAKE, None) == EINVAL
+    assert L.engram_probe_records(FAKE, 1 << 20, 0, 4, 1, FAKE + 4, None) == EINVAL
+    assert L.engram_probe_records(FAKE, 1 << 20, 0, -1, 1, FAKE, None) == EINVAL
+    assert L.engram_probe_records(FAKE, 1 << 20, 4, 4, 1, FAKE, None) == EUNSUPPORTED
+    assert L.engram_probe_records(FAKE, 200, 0, 4, 1, FAKE, None) == EINVAL
+    assert L.engram_probe_records(FAKE, 1 << 20, 3, 0, 1, FAKE, None) == OK
