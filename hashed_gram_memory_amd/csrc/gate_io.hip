@@ -9,8 +9,8 @@
 //   gather_rows_kernel      the 48 dequantised rows of each token, un-reduced;
 //   gather_weighted_kernel  the per-module sum with one caller weight per row
 //                           (a gate's output applied without a second pass).
-// Mapping as gather_reduce_kernel: one wave per (token, module), XCDs 0-3
-// module 0 and XCDs 4-7 module 1, rows read as 64 lanes x 4 B.
+// Mapping as gather_reduce_kernel: one wave per (token, module), block b
+// serving module b % 2, rows read as 64 lanes x 4 B.
 #include "row_sum.h"
 
 namespace engram {
@@ -21,9 +21,8 @@ __global__ __launch_bounds__(256) void gather_weighted_kernel(const GatherParams
                                                               const float* __restrict__ weights, uint32_t tok_base,
                                                               uint32_t n_tok, float* __restrict__ out) {
     const uint32_t b = blockIdx.x;
-    const uint32_t xcd = b & 7u;
-    const uint32_t module = xcd >> 2;
-    const uint32_t group = (b >> 3) * 4u + (xcd & 3u);
+    const uint32_t module = b & 1u;  // block b: module b % 2 of 4 consecutive items
+    const uint32_t group = b >> 1;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t tok = tok_base + group * 4u + wave;
@@ -43,9 +42,8 @@ template <int FMT>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const GatherParams P, const uint32_t* __restrict__ addr,
                                                           uint32_t tok_base, uint32_t n_tok, float* __restrict__ rows) {
     const uint32_t b = blockIdx.x;
-    const uint32_t xcd = b & 7u;
-    const uint32_t module = xcd >> 2;
-    const uint32_t group = (b >> 3) * 4u + (xcd & 3u);
+    const uint32_t module = b & 1u;  // block b: module b % 2 of 4 consecutive items
+    const uint32_t group = b >> 1;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t tok = tok_base + group * 4u + wave;

@@ -13,26 +13,26 @@
 // Mapping (gfx950, wave64):
 //   * one wavefront per (token, module); a row is one coalesced
 //     global_load_dword of 64 lanes x 4 B, lane l holding elements 4l..4l+3;
-//   * the 24 addresses of a (token, module) are contiguous: lane q < 24 loads
-//     address q, forms row q's base and loads row q's scale (or its 8-byte
-//     group of block scales), so the addresses and the 24 scales each take
-//     one vector load; row bases are broadcast from their lane one at a time
-//     (few scalar registers live: 8 waves per SIMD fit);
-//   * all 24 row loads are issued before the first is consumed, so a wave
-//     keeps 24 x 256 B in flight; with up to 8 waves per SIMD that is
-//     ~200 KB in flight per CU;
-//   * row loads carry the non-temporal hint: 84% of the rows of a 128K-token
-//     prompt are read once, and keeping them out of L2 leaves room for the
-//     reused rows and for the scale lines (every 4-byte scale read fetches a
-//     whole 128-byte line on gfx950);
+//   * the 24 addresses of a (token, module) are contiguous: lane q < 24
+//     loads address q (one vector load for all 24) and forms row q's base
+//     and its scale's address; the wave then broadcasts them one row at a
+//     time, so few scalar registers are live and 8 waves per SIMD fit;
+//   * each scale is a scalar load from its broadcast address (faster than
+//     one vector load that gathers the 24 scale lines across lanes);
+//   * all 24 row and scale loads are issued before the first is consumed, so
+//     a wave keeps 24 x 256 B of rows in flight;
+//   * cache policy by n-gram order: the order-2 rows, which a token stream
+//     repeats, are plain loads that L2 may keep; the order-3 and order-4
+//     rows, nearly all read once, are non-temporal (every 4-byte scale read
+//     still fetches a whole 128-byte line on gfx950);
 //   * decode with the gfx950 packed FP8 (OCP E4M3) -> fp32 conversion, then
 //     fused multiply-add into 4 fp32 accumulators per lane in ascending q
 //     (row_sum.h, shared with the fused lookup);
 //   * the 1 KiB result is written with non-temporal stores so output
 //     traffic does not evict table rows from L2 / MALL;
-//   * XCD-aware block order: the dispatcher hands block b to XCD b % 8; the
-//     grid is laid out so XCDs 0-3 serve module 0 and XCDs 4-7 module 1,
-//     which halves the set of sub-tables each XCD's L2 has to cache.
+//   * block b serves module b % 2 for 4 consecutive tokens.  (A layout that
+//     sent each module to its own half of the 8 XCDs, so each XCD's L2 saw
+//     half of the sub-tables, measured 1% slower.)
 #include "row_sum.h"
 
 namespace engram {
@@ -46,9 +46,8 @@ __global__ __launch_bounds__(256) void gather_reduce_kernel(const GatherParams P
                                                             const int32_t* __restrict__ n_unique,
                                                             float* __restrict__ out) {
     const uint32_t b = blockIdx.x;
-    const uint32_t xcd = b & 7u;
-    const uint32_t module = xcd >> 2;
-    const uint32_t group = (b >> 3) * 4u + (xcd & 3u);
+    const uint32_t module = b & 1u;  // block b: module b % 2 of 4 consecutive items
+    const uint32_t group = b >> 1;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t item = item_base + group * 4u + wave;

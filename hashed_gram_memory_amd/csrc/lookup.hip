@@ -8,8 +8,8 @@
 // This drops the 192-byte address write and read per token and one launch,
 // which is what a decode step of a few tokens is made of.
 //
-// Mapping: as gather_reduce_kernel (one wave per (token, module), XCDs 0-3
-// module 0, XCDs 4-7 module 1).  The window ids are wave-uniform; lane q < 24
+// Mapping: as gather_reduce_kernel (one wave per (token, module), block b
+// serving module b % 2).  The window ids are wave-uniform; lane q < 24
 // hashes row q of the module in parallel with the others, with the same
 // multiply-xor and modulus (a mask for power-of-two row counts) as
 // hash_kernel, and then owns that row in the lane-addressed loads.  The
@@ -38,9 +38,8 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
                                                      const int32_t* __restrict__ history, uint32_t tok_base,
                                                      uint32_t n_tok, uint32_t seq_len, float* __restrict__ out) {
     const uint32_t b = blockIdx.x;
-    const uint32_t xcd = b & 7u;
-    const uint32_t m = xcd >> 2;
-    const uint32_t group = (b >> 3) * 4u + (xcd & 3u);
+    const uint32_t m = b & 1u;  // block b: module b % 2 of 4 consecutive items
+    const uint32_t group = b >> 1;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t tok = tok_base + group * 4u + wave;

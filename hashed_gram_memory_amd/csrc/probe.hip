@@ -113,14 +113,13 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
-// Same mapping as gather_reduce_kernel (one wave per (token, module), XCD
-// split by module), rows only.
+// Same mapping as gather_reduce_kernel (one wave per (token, module), block b
+// serving module b % 2), rows only.
 __global__ __launch_bounds__(256) void rows_kernel(const GatherParams P, const uint32_t* __restrict__ addr,
                                                    uint32_t item_base, uint32_t n_items, float* __restrict__ out) {
     const uint32_t b = blockIdx.x;
-    const uint32_t xcd = b & 7u;
-    const uint32_t module = xcd >> 2;
-    const uint32_t group = (b >> 3) * 4u + (xcd & 3u);
+    const uint32_t module = b & 1u;  // block b: module b % 2 of 4 consecutive items
+    const uint32_t group = b >> 1;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t tok = item_base + group * 4u + wave;
