@@ -47,9 +47,14 @@ GATHER_SRCS = [os.path.join(ROOT, "hashed_gram_memory_amd", "csrc", f)
 
 
 def gather_source_sha256() -> str:
+    """sha256 of the gather kernel's code: its sources with // comments, blank lines and indentation removed,
+    so that editing a comment does not detach the stored counters from the kernel they were taken on."""
     h = hashlib.sha256()
     for f in GATHER_SRCS:
-        h.update(open(f, "rb").read())
+        for line in open(f, encoding="utf-8"):
+            code = line.split("//", 1)[0].strip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -4,12 +4,14 @@
 // Rows are 256 FP8 E4M3 codes [How to Run DeepSeek-V4.1-Flash: 510 GB, and
 // 203 GB of It Is a Lookup Table, section "Engram: the table that is never
 // multiplied"]; a wave reads one row as 64 lanes x 4 B, lane l holding
-// elements 4l..4l+3.  Two scale formats:
-//   ENGRAM_SCALE_F32_ROW       one fp32 per row (wave-uniform scalar load);
+// elements 4l..4l+3.  Two scale formats, both read with scalar loads (the
+// tables are read-only while a kernel runs, so the scalar cache may hold
+// them):
+//   ENGRAM_SCALE_F32_ROW       one fp32 per row;
 //   ENGRAM_SCALE_E8M0_BLOCK32  eight E8M0 exponents per row, one per 32
-//                              elements (the row's 8 bytes of scales; lane l
-//                              loads byte l/8).  An E8M0 byte e is
-//                              2^(e-127), and 255 is NaN.
+//                              elements (the row's 8 bytes of scales, one
+//                              8-byte load; lane l uses byte l/8).  An E8M0
+//                              byte e is 2^(e-127), and 255 is NaN.
 #pragma once
 
 #include "engram_internal.h"
