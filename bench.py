@@ -315,6 +315,32 @@ def main(argv=None) -> int:
         t_fused = _median_ms(torch, fused_step, stream, max(5, min(args.steps, 50)))
         fused = {"us_per_step": t_fused * 1e3, "tokens_per_s": n_tok / (t_fused / 1e3)}
 
+    # the gate-input calls on the first batch's addresses (one batch replayed): per-module sums with one
+    # weight per row, and the 48 dequantised rows un-reduced (fp32 [n_tok, 48, 256], 48 KiB per token)
+    scale_bytes = 48 * (8 if mx else 4)  # per token
+    gate = None
+    if not args.dedup and n_tok <= 131072:
+        b0 = batches[0]
+        hg.hash(plan, b0[1], b0[2], out=addr, stream=stream)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.token_seed + 7)
+        weights = torch.rand((n_tok, 48), generator=gen, device=dev)
+        rows_out = torch.empty((n_tok, 48, 256), dtype=torch.float32, device=dev)
+        t_w = _median_ms(torch, lambda: hg.gather_weighted(plan, addr, weights, out=out, stream=stream), stream, 10)
+        t_r = _median_ms(torch, lambda: hg.gather_rows(plan, addr, out=rows_out, stream=stream), stream, 5)
+        del rows_out, weights
+        w_bytes = n_tok * (48 * 256 + scale_bytes + 48 * 4 + 48 * 4 + 2 * 256 * 4)
+        r_bytes = n_tok * (48 * 256 + scale_bytes + 48 * 4 + 48 * 256 * 4)
+        gate = {
+            "ids": "first batch, replayed",
+            "gather_weighted_us": t_w * 1e3,
+            "gather_weighted_bytes_per_launch": w_bytes,
+            "gather_weighted_frac": w_bytes / (t_w / 1e3) / 1e9 / HBM_PEAK_GBPS,
+            "gather_rows_us": t_r * 1e3,
+            "gather_rows_bytes_per_launch": r_bytes,
+            "gather_rows_frac": r_bytes / (t_r / 1e3) / 1e9 / HBM_PEAK_GBPS,
+        }
+
     # distinct (sub-table, row) pairs of the first batch: the bytes a perfect cache would still fetch
     b0 = batches[0]
     hg.hash(plan, b0[1], b0[2], out=addr, stream=stream)
@@ -327,7 +353,6 @@ def main(argv=None) -> int:
     ms_per_step = wall / args.steps * 1e3
     tok_s = n_tok / (ms_per_step / 1e3)
     n_unique = int(groups.n_unique.item()) if args.dedup else None
-    scale_bytes = 48 * (8 if mx else 4)  # per token
     if args.dedup:
         # one lookup per group (rows, scales, addresses, its offsets pair) + one perm read and one
         # 2 KiB output store per token
@@ -390,6 +415,7 @@ def main(argv=None) -> int:
             "bytes": distinct * (256 + scale_bytes // 48) + n_tok * 2 * 256 * 4,
         },
         "fused_lookup": fused,
+        "gate_inputs": gate,
         "graph_replay": graph,
         "ceiling": ceiling,
         "cpu_baseline": base,
