@@ -60,8 +60,8 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const GatherParams P, 
 }
 
 template <int FMT>
-void launch_chunked(bool weighted, const GatherParams& p, const uint32_t* addr, const float* weights, uint32_t n_tok,
-                    float* out, hipStream_t stream) {
+hipError_t launch_chunked(bool weighted, const GatherParams& p, const uint32_t* addr, const float* weights,
+                          uint32_t n_tok, float* out, hipStream_t stream) {
     constexpr uint32_t kChunk = 1u << 24;
     for (uint32_t base = 0; base < n_tok; base += kChunk) {
         const uint32_t n = min(kChunk, n_tok - base);
@@ -72,8 +72,11 @@ void launch_chunked(bool weighted, const GatherParams& p, const uint32_t* addr, 
                                out);
         else
             hipLaunchKernelGGL((gather_rows_kernel<FMT>), grid, block, 0, stream, p, addr, base, base + n, out);
-        if (hipGetLastError() != hipSuccess) return;
+        // hipGetLastError also clears the error, so its value is what gets returned
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -82,10 +85,8 @@ hipError_t launch_gate_io(const GatherParams& p, const uint32_t* addr, const flo
                           float* out, hipStream_t stream) {
     const bool weighted = weights != nullptr;
     if (p.scale_format == ENGRAM_SCALE_E8M0_BLOCK32)
-        launch_chunked<ENGRAM_SCALE_E8M0_BLOCK32>(weighted, p, addr, weights, n_tok, out, stream);
-    else
-        launch_chunked<ENGRAM_SCALE_F32_ROW>(weighted, p, addr, weights, n_tok, out, stream);
-    return hipGetLastError();
+        return launch_chunked<ENGRAM_SCALE_E8M0_BLOCK32>(weighted, p, addr, weights, n_tok, out, stream);
+    return launch_chunked<ENGRAM_SCALE_F32_ROW>(weighted, p, addr, weights, n_tok, out, stream);
 }
 
 }  // namespace engram
