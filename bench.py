@@ -171,6 +171,9 @@ def main(argv=None) -> int:
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="read this many MiB of scratch before every timed step (evicts L2 and MALL without leaving "
                          "dirty lines; outside the per-kernel event pairs)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="use only the first N positions of every sequence (tokens per call = sequences x N), against "
+                         "the workload's full-size tables; 0: the whole workload")
     ap.add_argument("--id-batches", type=int, default=4,
                     help="rotate among this many seeded id batches of the same shape; the first is the workload's own "
                          "ids.  Rotation keeps a step from reading rows the previous step left in the caches (1: "
@@ -190,7 +193,8 @@ def main(argv=None) -> int:
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    n_tok = w.n_tok
+    seq_len = w.seq_len if args.tokens <= 0 else min(args.tokens, w.seq_len)
+    n_tok = w.n_seq * seq_len
 
     _log(f"allocating 48 x {w.rows} x 256 B tables")
     tables = torch.empty((48, w.rows, 256), dtype=torch.uint8, device=dev)
@@ -219,6 +223,7 @@ def main(argv=None) -> int:
                 hist = workloads.uniform_ids(w.n_seq, 3, w.token_seed + 100 * b + 1)
         else:
             ids, hist = workloads.make_ids(w, None if b == 0 else w.token_seed + 100 * b)
+        ids = np.ascontiguousarray(ids[:, :seq_len])
         batches.append((ids, torch.from_numpy(ids).to(dev), None if hist is None else torch.from_numpy(hist).to(dev)))
     addr = torch.empty((n_tok, 48), dtype=torch.uint32, device=dev)
     out = torch.empty((n_tok, 2, 256), dtype=torch.float32, device=dev)
@@ -384,6 +389,7 @@ def main(argv=None) -> int:
         "config": {
             "workload": (WORKLOAD_TEXT[args.workload]),
             "n_tok": n_tok,
+            "tokens_per_sequence": seq_len,
             "rows_per_subtable": w.rows,
             "scale_format": args.scale_format,
             "vocab_map": "seeded 129280 -> 99092" if args.vocab_map else None,
