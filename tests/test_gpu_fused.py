@@ -133,6 +133,44 @@ def test_launch_chunk_boundary():
     assert np.array_equal(got_fused, got)
 
 
+def _token_checksums(out):
+    """float64 sum of each token's 512 outputs, in chunks (no second full-size buffer)."""
+    step = 1 << 20
+    return torch.cat([out[i:i + step].reshape(-1, 512).double().sum(dim=1) for i in range(0, out.shape[0], step)])
+
+
+def test_batched_order_across_the_chunk_boundary():
+    """Two sequences of 2^23 + 40 tokens: the fused lookup visits them in 64-position tiles and splits its grid at
+    2^24 items, which is where the last, 40-position tile begins.  Every token's output must be the two-call one:
+    both runs write one buffer in turn and their per-token checksums (deterministic sums of bitwise-equal data)
+    must agree exactly, and a sample of tokens is compared element by element."""
+    n_seq, seq_len = 2, (1 << 23) + 40
+    _say(f"fused batched order, {n_seq} x {seq_len} tokens")
+    R = 512
+    host_t, host_c = workloads.dense_tables(809, R)
+    t, c = small_device_tables(host_t, host_c)
+    plan = lib().Plan(t, c)
+    rng = np.random.default_rng(25)
+    ids = rng.integers(0, 129280, size=(n_seq, seq_len), dtype=np.int64).astype(np.int32)
+    d_ids, _ = to_dev_ids(ids, None)
+    n_tok = n_seq * seq_len
+    sample = torch.from_numpy(np.unique(np.concatenate([
+        np.arange(0, 130), np.arange(seq_len - 100, seq_len + 100), np.arange(n_tok - 100, n_tok),
+        rng.integers(0, n_tok, 4000)]))).cuda()
+    out = lib().lookup(plan, d_ids)
+    fused_sum = _token_checksums(out)
+    fused_sample = out[sample].clone()
+    addr = lib().hash(plan, d_ids)
+    lib().gather_reduce(plan, addr, out=out)
+    torch.cuda.synchronize()
+    two_sum = _token_checksums(out)
+    two_sample = out[sample].clone()
+    del addr, out
+    torch.cuda.empty_cache()
+    assert torch.equal(fused_sample, two_sample)
+    assert torch.equal(fused_sum, two_sum)
+
+
 def test_one_plan_on_two_streams():
     """A plan is immutable: concurrent calls on two streams give the sequential results."""
     _say("one plan, two streams")
