@@ -318,7 +318,10 @@ def main(argv=None) -> int:
             hg.lookup(plan, b[1], b[2], out=out, stream=stream)
 
         t_fused = _median_ms(torch, fused_step, stream, max(5, min(args.steps, 50)))
-        fused = {"us_per_step": t_fused * 1e3, "tokens_per_s": n_tok / (t_fused / 1e3)}
+        # one id read per token (the window's other ids are cache hits), rows, scales, output
+        fused_bytes = n_tok * (4 + 48 * 256 + 48 * (8 if mx else 4) + 2 * 256 * 4)
+        fused = {"us_per_step": t_fused * 1e3, "tokens_per_s": n_tok / (t_fused / 1e3),
+                 "bytes_per_launch": fused_bytes, "frac": fused_bytes / (t_fused / 1e3) / 1e9 / HBM_PEAK_GBPS}
 
     # the gate-input calls on the first batch's addresses (one batch replayed): per-module sums with one
     # weight per row, and the 48 dequantised rows un-reduced (fp32 [n_tok, 48, 256], 48 KiB per token)
