@@ -236,7 +236,11 @@ int engram_gather_rows(engram_plan_t plan, const uint32_t* addr, int64_t n_tok, 
  * Fused lookup: engram_hash followed by engram_gather_reduce (direct mode)
  * in one launch, without the address buffer.  The addresses depend on the
  * ids alone [VRAM; GUIDE "Engram"], so each (token, module) computes its own
- * 24 rows and gathers them.  Bitwise identical to the two calls.
+ * 24 rows and gathers them.  Bitwise identical to the two calls.  A batch
+ * of sequences is visited in tiles of 64 positions, sequence by sequence
+ * within a tile, so sequences that share a prefix read each prefix row from
+ * L2 after its first fetch: passing such sequences in one call is cheaper
+ * than one call each.
  *
  *   ids, history, n_seq, seq_len   as for engram_hash.
  *   out       device fp32 [n_seq*seq_len][2][256], 16-byte aligned (output).
