@@ -11,10 +11,11 @@
 // Layout: a block covers 64 tokens with 6 waves, one per (module, order);
 // lane l of every wave is token l of the block.  A wave's 8 heads share the
 // (module, order), so its 32 multipliers and its 8 (R, magic) pairs are
-// wave-uniform scalar loads from the kernel arguments; the thread reads its
-// token's window (4 ids, cached across the 6 waves) and puts its 8
-// addresses into an LDS tile of the block's 64 x 48 addresses, which the
-// block then writes as one contiguous 12 KiB run with 16-byte stores.  The
+// wave-uniform scalar loads from the kernel arguments.  The block first
+// stages the 67 ids its windows read in LDS; each thread reads its token's
+// window from there and puts its 8 addresses into an LDS tile of the block's
+// 64 x 48 addresses, which the block then writes as one contiguous 12 KiB run
+// with 16-byte stores.  The
 // kernel is store-bound and small next to the gather (196 B per token
 // against ~14.7 KB).
 #include "engram_internal.h"
@@ -62,11 +63,33 @@ __global__ __launch_bounds__(384) void hash_kernel(const HashParams P, const int
     const uint32_t seq = tok / seq_len;
     const int32_t t = static_cast<int32_t>(tok - seq * seq_len);
 
+    // Stage the ids the block's windows read, flat positions first-3 ..
+    // first+63, once in LDS (with the vocabulary map already applied), so the
+    // 6 waves read their windows from LDS instead of 24 global loads per token.
+    const uint32_t first = blockIdx.x * 64u;
+    __shared__ uint32_t win_ids[64 + ENGRAM_MAX_ORDER - 1];
+    if (threadIdx.x < 64u + ENGRAM_MAX_ORDER - 1) {
+        const int64_t flat = static_cast<int64_t>(first) - (ENGRAM_MAX_ORDER - 1) + threadIdx.x;
+        uint32_t v = 0;
+        if (flat >= 0 && flat < static_cast<int64_t>(n_tok)) {
+            v = static_cast<uint32_t>(ids[flat]);
+            if (P.vocab_map) v = P.vocab_map[v];
+        }
+        win_ids[threadIdx.x] = v;
+    }
+    __syncthreads();
+
     // Window: w[k] = id at position t-k; before the sequence start, the
-    // caller's history (history[seq][2] is position -1) or id 0.
+    // caller's history (history[seq][2] is position -1) or id 0, each through
+    // the vocabulary map.
     uint64_t w[ENGRAM_MAX_ORDER];
 #pragma unroll
-    for (int k = 0; k < ENGRAM_MAX_ORDER; ++k) w[k] = window_id(ids, history, P.vocab_map, tok, seq, t, k);
+    for (int k = 0; k < ENGRAM_MAX_ORDER; ++k) {
+        if (t - k >= 0)
+            w[k] = win_ids[tok - k - first + (ENGRAM_MAX_ORDER - 1)];
+        else
+            w[k] = window_id(ids, history, P.vocab_map, tok, seq, t, k);
+    }
 
     const uint32_t mbase = wave * (ENGRAM_N_HEADS * ENGRAM_MAX_ORDER);  // multipliers of (m, order, head 0, k 0)
     const uint32_t s0 = m * kRowsPerModule + oi * ENGRAM_N_HEADS;
@@ -85,7 +108,6 @@ __global__ __launch_bounds__(384) void hash_kernel(const HashParams P, const int
     my[0] = make_uint4(a[0], a[1], a[2], a[3]);
     my[1] = make_uint4(a[4], a[5], a[6], a[7]);
     __syncthreads();
-    const uint32_t first = blockIdx.x * 64u;
     const uint32_t n_vec = (min(64u, n_tok - first) * kSub) / 4u;  // 16-byte words this block owns
     uint4* dst = reinterpret_cast<uint4*>(addr + static_cast<size_t>(first) * kSub);
     for (uint32_t i = threadIdx.x; i < n_vec; i += blockDim.x) dst[i] = stage[i];
