@@ -428,6 +428,12 @@ def main(argv=None) -> int:
         "graph_replay": graph,
         "ceiling": ceiling,
         "cpu_baseline": base,
+        "pages_context": {
+            "rows_per_token": 48,
+            "table_bytes_per_token": 12672,
+            "decode": "10 tokens/s needs ~120 KB/s of table reads",
+            "note": "figures the pages give for the whole model on other hardware, not an Engram kernel result",
+        },
     }
     if ceiling:
         rec["ceiling"]["gather_vs_read_ceiling"] = achieved / ceiling["stream_read_GBps"]
