@@ -33,7 +33,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr uint32_t kTile = 1024;          // elements per block per pass (4 sub-tiles)
-constexpr uint32_t kMaxBlocks = 1u << 21;  // (2^31 - 1) / 1024, rounded up
 
 struct Ids {
     const int32_t* ids;
@@ -64,11 +63,6 @@ __global__ __launch_bounds__(kThreads) void build_keys_kernel(Ids s, uint32_t n,
     klo[tok] = lo;
     khi[tok] = hi;
     val[tok] = static_cast<int32_t>(tok);
-}
-
-__device__ __forceinline__ uint32_t digit_at(uint64_t lo, uint64_t hi, int pass) {
-    return pass < 8 ? static_cast<uint32_t>(lo >> (8 * pass)) & 0xFFu
-                    : static_cast<uint32_t>(hi >> (8 * (pass - 8))) & 0xFFu;
 }
 
 // Lanes of this wave whose `valid` digit equals this lane's.
