@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_support import (addr_to_host, assert_within_tolerance, big_buffer, dummy_plan, lib, mark_buffer_dirty,
+from gpu_support import (addr_to_host, assert_within_tolerance, big_buffer, lib, mark_buffer_dirty,
                          sample_tokens, to_dev_ids)
 
 pytestmark = pytest.mark.gpu
