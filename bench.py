@@ -74,6 +74,14 @@ def _traffic(n_tok: int, id_batches: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _traffic_exact(n_tok: int, id_batches: int):
+    """Bytes per gather launch leaving L2 from the request-size counters (128- and 64-byte reads, 64-byte writes),
+    under the same kernel and run checks as the FETCH_SIZE/WRITE_SIZE figure."""
+    if _traffic(n_tok, id_batches) is None:
+        return None
+    return json.load(open(PMC_FILE)).get("request_sizes", {}).get("bytes_exact")
+
+
 def cpu_baseline(ids, rows: int, seed: int, sample_tokens: int):
     """The CPU oracle on the first ``sample_tokens`` tokens of the workload, full-size tables."""
     import oracle
@@ -370,6 +378,7 @@ def main(argv=None) -> int:
     achieved = gather_bytes / (gather_ms / 1e3) / 1e9
     plain = not (args.dedup or mx or args.vocab_map or args.prime_rows or args.uniform_ids or args.flush_mib)
     traffic = _traffic(n_tok, args.id_batches) if args.workload == 4 and plain else None
+    traffic_exact = _traffic_exact(n_tok, args.id_batches) if args.workload == 4 and plain else None
 
     base = None
     if args.cpu_sample > 0 and args.workload == 4:
@@ -412,6 +421,12 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
+        },
+        "traffic_by_request_size": None if traffic_exact is None else {
+            "bytes": traffic_exact,
+            "GBps": traffic_exact / (gather_ms / 1e3) / 1e9,
+            "note": "exact bytes leaving L2 from the request-size counters; roofline.traffic follows the FETCH_SIZE x "
+                    "copy-calibration method, which counts the 64-byte scale requests as 128 bytes",
         },
         "gather_ms": gather_ms,
         "hash_ms": hash_ms,
