@@ -249,8 +249,18 @@ def main(argv=None) -> int:
         if args.dedup:
             hg.dedup(plan, b[1], b[2], workspace=ws, groups=groups, stream=stream)
 
+    # a batch of sequences is gathered in the batch order (engram_gather_reduce_batched): same results, and
+    # sequences that share a prefix read it from L2
+    batched = not args.dedup and w.n_seq > 1
+
+    def gather(stream=None):
+        if batched:
+            hg.gather_reduce_batched(plan, addr, w.n_seq, out=out, stream=stream)
+        else:
+            hg.gather_reduce(plan, addr, out=out, groups=groups, stream=stream)
+
     def gather_phase():
-        hg.gather_reduce(plan, addr, out=out, groups=groups, stream=stream)
+        gather(stream)
 
     def step(i):
         hash_phase(i)
@@ -295,7 +305,7 @@ def main(argv=None) -> int:
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             hg.hash(plan, b0[1], b0[2], out=addr)
-            hg.gather_reduce(plan, addr, out=out)
+            gather()
             hg.lookup(plan, b0[1], b0[2], out=out)
         stream.wait_stream(side)
         # 20 steps per graph: one replay shows the device-side time of back-to-back steps
@@ -305,7 +315,7 @@ def main(argv=None) -> int:
             for j in range(per_graph):
                 b = batches[j % len(batches)]
                 hg.hash(plan, b[1], b[2], out=addr)
-                hg.gather_reduce(plan, addr, out=out)
+                gather()
         with torch.cuda.graph(g_fused):
             for j in range(per_graph):
                 b = batches[j % len(batches)]
@@ -410,12 +420,13 @@ def main(argv=None) -> int:
             "flush_mib_per_step": args.flush_mib,
             "id_batches": args.id_batches,
             "step": "engram_hash + engram_dedup + engram_gather_reduce (dedup mode)" if args.dedup
+                    else "engram_hash + engram_gather_reduce_batched" if batched
                     else "engram_hash + engram_gather_reduce",
             "n_unique": n_unique,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gather_reduce_kernel",
+            "kernel": "gather_batched_kernel" if batched else "gather_reduce_kernel",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

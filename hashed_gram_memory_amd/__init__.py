@@ -74,6 +74,7 @@ def _load():
         "engram_hash": [P, VP, VP, I64, I64, VP, VP],
         "engram_gather_reduce": [P, VP, I64, VP, VP, VP, VP, VP],
         "engram_lookup": [P, VP, VP, I64, I64, VP, VP],
+        "engram_gather_reduce_batched": [P, VP, I64, I64, VP, VP],
         "engram_gather_weighted": [P, VP, I64, VP, VP, VP],
         "engram_gather_rows": [P, VP, I64, VP, VP],
         "engram_dedup_workspace": [I64, ctypes.POINTER(ctypes.c_size_t)],
@@ -299,6 +300,25 @@ def lookup(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, o
                             None if history is None else _dev(history, torch.int32, "history"), n_seq, seq_len,
                             _dev(out, torch.float32, "out"), _stream(stream))
     _check(st, "engram_lookup")
+    return out
+
+
+def gather_reduce_batched(plan: Plan, addr: torch.Tensor, n_seq: int, out: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """engram_gather_reduce over a batch of ``n_seq`` equal-length sequences (addr [n_seq*seq_len, 48] in token order),
+    visiting tokens in the batch order: fp32 [n_tok, 2, 256] (engram_gather_reduce_batched)."""
+    if addr.dim() != 2 or addr.shape[1] != N_SUB:
+        raise ValueError("addr must be [n_tok, 48]")
+    n_tok = addr.shape[0]
+    if n_seq <= 0 or n_tok % n_seq:
+        raise ValueError("n_seq must divide the token count")
+    if out is None:
+        out = torch.empty((n_tok, N_MODULES, ROW_BYTES), dtype=torch.float32, device=addr.device)
+    elif tuple(out.shape) != (n_tok, N_MODULES, ROW_BYTES):
+        raise ValueError("out must be [n_tok, 2, 256]")
+    st = _lib.engram_gather_reduce_batched(plan.handle, _dev(addr, torch.uint32, "addr"), n_seq, n_tok // n_seq,
+                                           _dev(out, torch.float32, "out"), _stream(stream))
+    _check(st, "engram_gather_reduce_batched")
     return out
 
 

@@ -6,6 +6,7 @@
 #include <new>
 #include <string.h>
 
+#include "batch_order.h"
 #include "engram_internal.h"
 
 using namespace engram;
@@ -124,6 +125,19 @@ int engram_gather_reduce(engram_plan_t p, const uint32_t* addr, int64_t n_tok, c
         return ENGRAM_EINVAL;
     hipError_t e = launch_gather_reduce(p->gather, addr, uint32_t(n_tok), perm, offsets, n_unique, out,
                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
+}
+
+int engram_gather_reduce_batched(engram_plan_t p, const uint32_t* addr, int64_t n_seq, int64_t seq_len, float* out,
+                                 void* stream) {
+    if (!valid_plan(p)) return ENGRAM_EINVAL;
+    int64_t n_tok = 0;
+    int st = check_tokens(n_seq, seq_len, &n_tok);
+    if (st != ENGRAM_OK) return st;
+    if (n_tok == 0) return ENGRAM_OK;
+    if (!addr || !out || !aligned(addr, 16) || !aligned(out, 16)) return ENGRAM_EINVAL;
+    hipError_t e = launch_gather_batched(p->gather, addr, uint32_t(n_tok), uint32_t(seq_len), out,
+                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
 }
 

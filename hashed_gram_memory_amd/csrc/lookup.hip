@@ -8,17 +8,17 @@
 // This drops the 192-byte address write and read per token and one launch,
 // which is what a decode step of a few tokens is made of.
 //
-// Mapping: one wave per (token, module).  In a batch of sequences the
-// tokens are visited in tiles of 64 positions, sequence by sequence within a
-// tile, so that sequences sharing a prefix read each prefix row from one
-// XCD's L2 within a short time (with one sequence this is plain token
-// order).  The window ids are wave-uniform; lane q < 24
+// Mapping: one wave per (token, module), tokens visited in the batch order
+// of batch_order.h (tiles of 64 positions, sequence by sequence within a
+// tile; plain token order for one sequence).  The window ids are
+// wave-uniform; lane q < 24
 // hashes row q of the module in parallel with the others, with the same
 // multiply-xor and modulus (a mask for power-of-two row counts) as
 // hash_kernel, and then owns that row in the lane-addressed loads.  The
 // accumulation is the fused multiply-add sequence of gather_reduce_kernel, so
 // the result is bitwise identical to engram_hash followed by
 // engram_gather_reduce.
+#include "batch_order.h"
 #include "row_sum.h"
 
 namespace engram {
@@ -39,8 +39,7 @@ __device__ __forceinline__ uint32_t mod_rows(uint64_t x, uint64_t R, uint64_t ma
 template <bool POW2, int FMT>
 __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const int32_t* __restrict__ ids,
                                                      const int32_t* __restrict__ history, uint32_t item_base,
-                                                     uint32_t item_end, uint32_t n_seq, uint32_t seq_len,
-                                                     uint32_t tile, float* __restrict__ out) {
+                                                     uint32_t item_end, BatchOrder batch, float* __restrict__ out) {
     const uint32_t b = blockIdx.x;
     const uint32_t m = b & 1u;  // block b: module b % 2 of 4 consecutive items
     const uint32_t group = b >> 1;
@@ -48,23 +47,8 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t item = item_base + group * 4u + wave;
     if (item >= item_end) return;
-
-    // Item order: positions in tiles of `tile` (64, or the whole sequence if
-    // shorter); within a tile, sequence by sequence.  Consecutive items are
-    // consecutive positions of one sequence (contiguous output), and the same
-    // position of the next sequence comes `tile` items later: 32 blocks for a
-    // 64-position tile, which the round-robin dispatcher sends to the same
-    // XCD.  Sequences that share a prefix therefore read each prefix row from
-    // that XCD's L2 after the first fetch.  With one sequence this is plain
-    // token order.
-    const uint32_t span = tile * n_seq;  // items per tile of positions (<= n_tok: tile <= seq_len)
-    const uint32_t tile_idx = item / span;
-    const uint32_t p0 = tile_idx * tile;
-    const uint32_t width = min(tile, seq_len - p0);  // the last tile may be narrower
-    const uint32_t rem = item - tile_idx * span;
-    const uint32_t seq = rem / width;
-    const uint32_t t = p0 + (rem - seq * width);  // position in the sequence
-    const uint32_t tok = seq * seq_len + t;
+    uint32_t seq, t;
+    const uint32_t tok = batched_token(item, batch, &seq, &t);
 
     // Window of the token (wave-uniform): w[k] = id k positions back, else history, else 0.
     uint64_t w[ENGRAM_MAX_ORDER];
@@ -102,28 +86,26 @@ hipError_t launch_lookup(const HashParams& h, const GatherParams& g, const int32
     bool pow2 = true;
     for (int s = 0; s < kSub; ++s) pow2 = pow2 && (h.rows[s] & (h.rows[s] - 1u)) == 0;
     // Launches cover at most 2^24 items so the grid stays far below 2^32
-    // threads.  64-position tiles measured fastest on 64 sequences sharing a
-    // 4,096-token prefix (32: 1.02x, 128: 1.04x, 256: 1.12x the time).
+    // threads.
     constexpr uint32_t kChunk = 1u << 24;
     const bool mx = g.scale_format == ENGRAM_SCALE_E8M0_BLOCK32;
-    const uint32_t n_seq = n_tok / seq_len;
-    const uint32_t tile = min(64u, seq_len);
+    const BatchOrder batch = batch_order(n_tok, seq_len);
     for (uint32_t base = 0; base < n_tok; base += kChunk) {
         const uint32_t n = min(kChunk, n_tok - base);
         const uint32_t groups = ((n + 3u) / 4u + 3u) & ~3u;
         const dim3 grid(2u * groups), block(256);
         if (pow2 && mx)
             hipLaunchKernelGGL((lookup_kernel<true, ENGRAM_SCALE_E8M0_BLOCK32>), grid, block, 0, stream, p, ids, history,
-                               base, base + n, n_seq, seq_len, tile, out);
+                               base, base + n, batch, out);
         else if (pow2)
             hipLaunchKernelGGL((lookup_kernel<true, ENGRAM_SCALE_F32_ROW>), grid, block, 0, stream, p, ids, history, base,
-                               base + n, n_seq, seq_len, tile, out);
+                               base + n, batch, out);
         else if (mx)
             hipLaunchKernelGGL((lookup_kernel<false, ENGRAM_SCALE_E8M0_BLOCK32>), grid, block, 0, stream, p, ids,
-                               history, base, base + n, n_seq, seq_len, tile, out);
+                               history, base, base + n, batch, out);
         else
             hipLaunchKernelGGL((lookup_kernel<false, ENGRAM_SCALE_F32_ROW>), grid, block, 0, stream, p, ids, history,
-                               base, base + n, n_seq, seq_len, tile, out);
+                               base, base + n, batch, out);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

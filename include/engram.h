@@ -208,6 +208,24 @@ int engram_gather_reduce(engram_plan_t plan, const uint32_t* addr, int64_t n_tok
                          const int32_t* n_unique, float* out, void* stream);
 
 /*
+ * engram_gather_reduce in direct mode for a batch of n_seq sequences of
+ * seq_len tokens whose addresses engram_hash wrote (addr[n_seq*seq_len][48],
+ * token-major).  Same results, bitwise; the tokens are visited in tiles of 64
+ * positions, sequence by sequence within a tile, so that sequences sharing a
+ * prefix read each prefix row from L2 after its first fetch (the pages hash
+ * every address before the lookup [VRAM; GUIDE "Engram"], and batched prompts
+ * often share a system prefix).
+ *
+ *   addr     device uint32 [n_seq*seq_len][48], 16-byte aligned.
+ *   out      device fp32 [n_seq*seq_len][2][256], 16-byte aligned (output).
+ *
+ * n_seq*seq_len == 0 is a no-op.  Errors: EINVAL (NULL/misaligned pointer,
+ * negative count), ERANGE (n_seq*seq_len above 2^31 - 1).
+ */
+int engram_gather_reduce_batched(engram_plan_t plan, const uint32_t* addr, int64_t n_seq, int64_t seq_len,
+                                 float* out, void* stream);
+
+/*
  * Inputs for the learned gate that follows the lookup: each retrieved row is
  * weighed against the hidden state before the module's rows are combined
  * [GUIDE "The architecture", "Engram"].  The gate itself (trained weights,

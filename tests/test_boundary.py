@@ -297,3 +297,16 @@ def test_probe_records_validation(hg):
     assert L.engram_probe_records(FAKE, 1 << 20, 4, 4, 1, FAKE, None) == EUNSUPPORTED
     assert L.engram_probe_records(FAKE, 200, 0, 4, 1, FAKE, None) == EINVAL
     assert L.engram_probe_records(FAKE, 1 << 20, 3, 0, 1, FAKE, None) == OK
+
+
+def test_gather_reduce_batched_validation(hg, plan):
+    L = hg.lib()
+    assert L.engram_gather_reduce_batched(None, FAKE, 1, 1, FAKE, None) == EINVAL
+    assert L.engram_gather_reduce_batched(plan, FAKE, 0, 5, FAKE, None) == OK
+    assert L.engram_gather_reduce_batched(plan, FAKE, 5, 0, FAKE, None) == OK
+    assert L.engram_gather_reduce_batched(plan, FAKE, -1, 5, FAKE, None) == EINVAL
+    assert L.engram_gather_reduce_batched(plan, FAKE, 2, -5, FAKE, None) == EINVAL
+    assert L.engram_gather_reduce_batched(plan, FAKE, 1 << 16, 1 << 16, FAKE, None) == ERANGE
+    assert L.engram_gather_reduce_batched(plan, None, 2, 3, FAKE, None) == EINVAL
+    assert L.engram_gather_reduce_batched(plan, FAKE + 4, 2, 3, FAKE, None) == EINVAL
+    assert L.engram_gather_reduce_batched(plan, FAKE, 2, 3, FAKE + 8, None) == EINVAL
