@@ -16,7 +16,8 @@
  * 2, 3 and 4 of the token-id stream with 8 independent heads and read one
  * row per (order, head): 24 rows per module, 48 per token [GUIDE "Engram";
  * VRAM].  Rows are 256 bytes of FP8 [GUIDE "Engram"; REQ]; each carries one
- * fp32 scale here.  The row addresses depend on the token ids alone, so the
+ * fp32 scale, or 8 E8M0 exponents (one per 32 elements), as the plan says.
+ * The row addresses depend on the token ids alone, so the
  * whole prompt is hashed before any row is read [VRAM; GUIDE "Engram"]: the
  * library exposes the hash and the gather as separate calls.  The 24
  * dequantised rows of a module are summed into one fp32 vector of 256
