@@ -8,11 +8,14 @@
  * ... (one sequence of n_tok tokens, mod 129,280), gathers and sums, runs the
  * fused lookup too, and writes to <out.bin>:
  *     int32 ids[n_tok] | uint32 addr[n_tok][48] | float out[n_tok][2][256] | float fused[n_tok][2][256]
- * Exit status 0 on success; any failing call prints its status and exits 1.
+ * It also gathers the same addresses with engram_gather_reduce_batched and
+ * checks that the result equals the flat gather's bit for bit.
+ * Exit status 0 on success; any failing call or check prints why and exits 1.
  */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <hip/hip_runtime_api.h>
 
@@ -75,25 +78,36 @@ int main(int argc, char** argv) {
     for (int64_t i = 0; i < n_tok; ++i) h_ids[i] = (int32_t)((i * 7) % 129280);
     int32_t* ids;
     uint32_t* addr;
-    float *out, *fused;
+    float *out, *fused, *batched;
     const size_t out_bytes = (size_t)n_tok * 2 * ENGRAM_ROW_BYTES * sizeof(float);
     CHECK_HIP(hipMalloc((void**)&ids, n_tok * sizeof(int32_t)));
     CHECK_HIP(hipMalloc((void**)&addr, n_tok * ENGRAM_N_SUB * sizeof(uint32_t)));
     CHECK_HIP(hipMalloc((void**)&out, out_bytes));
     CHECK_HIP(hipMalloc((void**)&fused, out_bytes));
+    CHECK_HIP(hipMalloc((void**)&batched, out_bytes));
     CHECK_HIP(hipMemcpyAsync(ids, h_ids, n_tok * sizeof(int32_t), hipMemcpyHostToDevice, stream));
 
     CHECK_ENGRAM(engram_hash(plan, ids, NULL, 1, n_tok, addr, stream));
     CHECK_ENGRAM(engram_gather_reduce(plan, addr, n_tok, NULL, NULL, NULL, out, stream));
     CHECK_ENGRAM(engram_lookup(plan, ids, NULL, 1, n_tok, fused, stream));
+    /* the same addresses gathered in the batch order, split into 7 equal sequences when the count allows:
+       only the visiting order differs, so the result must be the flat gather's, bit for bit */
+    const int64_t n_seq = n_tok % 7 == 0 ? 7 : 1;
+    CHECK_ENGRAM(engram_gather_reduce_batched(plan, addr, n_seq, n_tok / n_seq, batched, stream));
 
     uint32_t* h_addr = (uint32_t*)malloc(n_tok * ENGRAM_N_SUB * sizeof(uint32_t));
     float* h_out = (float*)malloc(out_bytes);
     float* h_fused = (float*)malloc(out_bytes);
+    float* h_batched = (float*)malloc(out_bytes);
     CHECK_HIP(hipMemcpyAsync(h_addr, addr, n_tok * ENGRAM_N_SUB * sizeof(uint32_t), hipMemcpyDeviceToHost, stream));
     CHECK_HIP(hipMemcpyAsync(h_out, out, out_bytes, hipMemcpyDeviceToHost, stream));
     CHECK_HIP(hipMemcpyAsync(h_fused, fused, out_bytes, hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipMemcpyAsync(h_batched, batched, out_bytes, hipMemcpyDeviceToHost, stream));
     CHECK_HIP(hipStreamSynchronize(stream));
+    if (memcmp(h_batched, h_out, out_bytes) != 0) {
+        fprintf(stderr, "engram_gather_reduce_batched differs from engram_gather_reduce\n");
+        return 1;
+    }
 
     FILE* f = fopen(argv[1], "wb");
     if (!f) return 1;
@@ -108,6 +122,7 @@ int main(int argc, char** argv) {
     CHECK_HIP(hipFree(addr));
     CHECK_HIP(hipFree(out));
     CHECK_HIP(hipFree(fused));
+    CHECK_HIP(hipFree(batched));
     CHECK_HIP(hipFree(tab));
     CHECK_HIP(hipFree(sc));
     CHECK_HIP(hipStreamDestroy(stream));
@@ -115,6 +130,7 @@ int main(int argc, char** argv) {
     free(h_addr);
     free(h_out);
     free(h_fused);
+    free(h_batched);
     printf("c_abi_demo ok: %lld tokens\n", (long long)n_tok);
     return 0;
 }
