@@ -29,6 +29,7 @@ BYTES_PER_TOKEN = {  # algorithmic bytes of engram_gather_reduce per token
     "rows": 48 * 256, "scales": 48 * 4, "addresses": 48 * 4, "output": 2 * 256 * 4}
 GATHER_BYTES_PER_TOKEN = sum(BYTES_PER_TOKEN.values())  # 14,720
 HASH_BYTES_PER_TOKEN = 4 + 48 * 4  # id in, addresses out
+MAX_CPU_WORKERS = 16  # a GPU's share of the host's cores
 WORKLOAD_TEXT = {
     1: "tiny: 1 x 512 uniform ids in [0, 1024); 48 sub-tables x 4096 rows x 256 B FP8 E4M3 + fp32 row scales",
     2: ("decode: 64 sequences x 1 new token against a 3-token history, Zipf(1.1) ids over 129280; 48 sub-tables x "
@@ -82,31 +83,112 @@ def _traffic_exact(n_tok: int, id_batches: int):
     return json.load(open(PMC_FILE)).get("request_sizes", {}).get("bytes_exact")
 
 
-def cpu_baseline(ids, rows: int, seed: int, sample_tokens: int):
-    """The CPU oracle on the first ``sample_tokens`` tokens of the workload, full-size tables."""
+def _oracle_worker(pieces, rows: int, seed: int, dense: bool, barrier, queue) -> None:
+    """One CPU worker (a spawned process that never touches the GPU): the oracle over its pieces of the workload.
+
+    Untimed preparation: the host tables (dense for small row counts; otherwise a lazily committed full-size
+    mapping with only the rows its tokens read filled in).  Timed, after every worker is ready: windows, hash
+    and gather-reduce of each piece."""
     import oracle
     import workloads
 
-    sub_ids = np.ascontiguousarray(ids[:, :sample_tokens])
     mult = oracle.multipliers()
-    addr = oracle.hash_addresses(oracle.windows(sub_ids), mult, [rows] * 48)
-    host = workloads.SparseHostTables(seed, rows)
+    rows48 = [rows] * 48
+    host = None
     try:
-        host.materialise(addr)  # input preparation, untimed
+        if dense:
+            tabs, scs = workloads.dense_tables(seed, rows)
+        else:
+            host = workloads.SparseHostTables(seed, rows)
+            for ids, hist in pieces:
+                host.materialise(oracle.hash_addresses(oracle.windows(ids, hist), mult, rows48))
+            tabs, scs = host.tables, host.scales
+        barrier.wait()
         t0 = time.perf_counter()
-        a = oracle.hash_addresses(oracle.windows(sub_ids), mult, [rows] * 48)
-        oracle.gather_reduce(host.tables, host.scales, a)
-        dt = time.perf_counter() - t0
+        n = 0
+        for ids, hist in pieces:
+            a = oracle.hash_addresses(oracle.windows(ids, hist), mult, rows48)
+            oracle.gather_reduce(tabs, scs, a)
+            n += ids.size
+        t1 = time.perf_counter()
+        queue.put((t0, t1, n))
+    except Exception as e:  # report instead of leaving the parent waiting
+        queue.put(("error", repr(e), 0))
+        barrier.abort()
     finally:
-        host.close()
+        if host is not None:
+            host.close()
+
+
+def _split_tokens(ids, hist, workers: int):
+    """Token pieces for ``workers`` processes: whole sequences when there are enough of them, else contiguous
+    chunks of each sequence, each carrying the 3 ids before it as its history (pad 0 at the sequence start)."""
+    n_seq, seq_len = ids.shape
+    if n_seq >= workers:
+        b = np.linspace(0, n_seq, workers + 1).astype(int)
+        return [[(ids[lo:hi], None if hist is None else hist[lo:hi])] for lo, hi in zip(b[:-1], b[1:]) if hi > lo]
+    per = [[] for _ in range(workers)]
+    for s in range(n_seq):
+        pad = hist[s] if hist is not None else np.zeros(3, np.int32)
+        ext = np.concatenate([pad, ids[s]]).astype(np.int32)  # ext[3 + p] is position p
+        b = np.linspace(0, seq_len, workers + 1).astype(int)
+        for w, (lo, hi) in enumerate(zip(b[:-1], b[1:])):
+            if hi > lo:
+                per[w].append((np.ascontiguousarray(ids[s:s + 1, lo:hi]), np.ascontiguousarray(ext[lo:lo + 3][None])))
+    return [p for p in per if p]
+
+
+def _time_oracle(ids, hist, rows: int, seed: int, workers: int) -> dict:
+    import multiprocessing as mp
+
+    ctx = mp.get_context("spawn")  # fresh interpreters: nothing of this process's GPU state is inherited
+    parts = _split_tokens(ids, hist, workers)
+    barrier, queue = ctx.Barrier(len(parts)), ctx.Queue()
+    dense = rows <= 4096
+    procs = [ctx.Process(target=_oracle_worker, args=(p, rows, seed, dense, barrier, queue)) for p in parts]
+    for p in procs:
+        p.start()
+    res = [queue.get(timeout=600) for _ in procs]
+    for p in procs:
+        p.join(timeout=60)
+    errors = [r for r in res if r[0] == "error"]
+    if errors:
+        raise RuntimeError(f"oracle worker failed: {errors[0][1]}")
+    wall = max(r[1] for r in res) - min(r[0] for r in res)
+    n = sum(r[2] for r in res)
+    return {"tokens": n, "seconds": wall, "tokens_per_s": n / wall, "processes": len(parts)}
+
+
+def cpu_baseline(keys, workers: int, tokens4: int) -> dict:
+    """The CPU oracle (numpy, float64) on whole workloads, timed with 1 process and with ``workers`` processes that
+    split the tokens.  Workload 4 is limited to its first ``tokens4`` tokens."""
+    import workloads
+
+    per = {}
+    for key in keys:
+        w = workloads.WORKLOADS[key]
+        ids, hist = workloads.make_ids(w)
+        if key == 4:
+            ids = np.ascontiguousarray(ids[:, :tokens4])
+        _log(f"cpu baseline: oracle on workload {key} ({ids.size} tokens), 1 and {workers} processes")
+        one = _time_oracle(ids, hist, w.rows, w.table_seed, 1)
+        many = _time_oracle(ids, hist, w.rows, w.table_seed, workers)
+        per[str(key)] = {"tokens": int(ids.size), "rows_per_subtable": w.rows, "cores_1": one, "cores_all": many}
+    head = per.get("4") or per[str(keys[-1])]
     return {
-        "value": sample_tokens / dt,
+        "value": head["cores_all"]["tokens_per_s"],
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"first {sample_tokens} tokens of the 131072-token Zipf stream: oracle windows + hash + "
-                   f"gather-reduce (numpy, float64) against full-size 48 x 2^{rows.bit_length() - 1} host tables "
-                   f"(only touched rows resident); {dt:.1f} s"),
+        "cores_1": head["cores_1"]["tokens_per_s"],
+        "cores_all": head["cores_all"]["tokens_per_s"],
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "per_workload": per,
+        "sample": (f"workload {'4' if '4' in per else keys[-1]}, {head['tokens']} tokens: oracle windows + hash + "
+                   f"gather-reduce (numpy, float64) against host tables (full size; only the rows read are "
+                   f"resident), tokens split over {workers} spawned processes (value) and in 1 process (cores_1); "
+                   f"workloads {', '.join(per)} in per_workload, whole inputs"
+                   + (f" (workload 4: first {tokens4} tokens)" if '4' in per else "")),
     }
 
 
@@ -156,12 +238,63 @@ def measure_ceiling(hg, torch, plan, tables, addr, out, stream):
     }
 
 
+def measure_controls(hg, torch, workloads, plan, w, batches, addr, out, stream, seq_len: int, gather_bytes: int,
+                     launches: int = 20, flush_mib: int = 1024) -> dict:
+    """Two control timings of engram_gather_reduce (HIP events around each launch, mean over the launches).
+
+    uniform_ids: 4 batches of ids uniform over the vocabulary, hashed ahead, gathered in turn: no Zipf row reuse.
+    flushed: the workload's own batches, with a 1 GiB read between launches, so every launch starts with L2
+    and the MALL holding none of the rows it reads."""
+    dev = addr.device
+    uni = []
+    for b in range(4):
+        ids = np.ascontiguousarray(workloads.uniform_ids(w.n_seq, w.seq_len, w.token_seed + 9000 + b)[:, :seq_len])
+        a = torch.empty_like(addr)
+        hg.hash(plan, torch.from_numpy(ids).to(dev), None, out=a, stream=stream)
+        uni.append(a)
+    for a in uni:  # warm-up
+        hg.gather_reduce(plan, a, out=out, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record(stream)
+        hg.gather_reduce(plan, uni[i % 4], out=out, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t_uni = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    del uni
+    flush = torch.ones(flush_mib << 20, dtype=torch.uint8, device=dev)
+    sink = torch.zeros((), dtype=torch.uint8, device=dev)
+    for i, (e0, e1) in enumerate(ev):
+        b = batches[i % len(batches)]
+        hg.hash(plan, b[1], b[2], out=addr, stream=stream)
+        sink.copy_(flush.max())
+        e0.record(stream)
+        hg.gather_reduce(plan, addr, out=out, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t_flush = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    del flush
+
+    def rec(t_ms, what):
+        gbps = gather_bytes / (t_ms / 1e3) / 1e9
+        return {"gather_us": t_ms * 1e3, "achieved_GBps": gbps, "frac": gbps / HBM_PEAK_GBPS, "ids": what}
+
+    return {"launches": launches,
+            "uniform_ids": rec(t_uni, "4 batches uniform over 129280, hashed ahead, gathered in turn"),
+            "flushed": rec(t_flush, f"the workload's batches with a {flush_mib} MiB read before every launch")}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-sample", type=int, default=131072, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=131072,
+                    help="tokens of workload 4 in the CPU oracle baseline (0: skip the baseline)")
+    ap.add_argument("--cpu-workloads", default="1,2,3,4",
+                    help="workloads the CPU oracle baseline times, with 1 process and with all cores")
+    ap.add_argument("--no-controls", action="store_true",
+                    help="skip the uniform-id and cache-flushed control timings of the gather")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
@@ -296,6 +429,10 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    controls = None
+    if args.workload == 4 and not (args.no_controls or args.dedup or args.uniform_ids or args.flush_mib):
+        controls = measure_controls(hg, torch, workloads, plan, w, batches, addr, out, stream, seq_len,
+                                    (GATHER_BYTES_PER_TOKEN - 48 * 4 + 48 * (8 if mx else 4)) * n_tok)
     ceiling = None if args.no_ceiling or args.dedup else measure_ceiling(hg, torch, plan, tables, addr, out, stream)
     graph = None
     if not args.dedup:
@@ -323,7 +460,8 @@ def main(argv=None) -> int:
         reps = 5
         t_two = _median_ms(torch, g_two.replay, stream, reps) / per_graph
         t_fused = _median_ms(torch, g_fused.replay, stream, reps) / per_graph
-        graph = {"steps_per_graph": per_graph, "two_call_us_per_step": t_two * 1e3, "fused_us_per_step": t_fused * 1e3}
+        graph = {"steps_per_graph": per_graph, "two_call_us_per_step": t_two * 1e3, "fused_us_per_step": t_fused * 1e3,
+                 "two_call_tokens_per_s": n_tok / (t_two / 1e3), "fused_tokens_per_s": n_tok / (t_fused / 1e3)}
         del g_two, g_fused
     fused = None
     if not args.dedup:
@@ -387,13 +525,14 @@ def main(argv=None) -> int:
         gather_bytes = (GATHER_BYTES_PER_TOKEN - 48 * 4 + scale_bytes) * n_tok
     achieved = gather_bytes / (gather_ms / 1e3) / 1e9
     plain = not (args.dedup or mx or args.vocab_map or args.prime_rows or args.uniform_ids or args.flush_mib)
-    traffic = _traffic(n_tok, args.id_batches) if args.workload == 4 and plain else None
-    traffic_exact = _traffic_exact(n_tok, args.id_batches) if args.workload == 4 and plain else None
+    traffic_fetch = _traffic(n_tok, args.id_batches) if args.workload == 4 and plain else None
+    traffic = _traffic_exact(n_tok, args.id_batches) if args.workload == 4 and plain else None
 
     base = None
     if args.cpu_sample > 0 and args.workload == 4:
-        _log(f"cpu baseline: oracle on {args.cpu_sample} tokens")
-        base = cpu_baseline(batches[0][0], w.rows, w.table_seed, min(args.cpu_sample, n_tok))
+        workers = max(1, min(len(os.sched_getaffinity(0)), MAX_CPU_WORKERS))
+        keys = [int(k) for k in args.cpu_workloads.split(",") if k.strip()]
+        base = cpu_baseline(keys, workers, min(args.cpu_sample, n_tok))
 
     rec = {
         "metric": "Engram lookup tokens/sec and achieved gather HBM GB/s (% of peak), 1 MI355X",
@@ -433,12 +572,19 @@ def main(argv=None) -> int:
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
         },
-        "traffic_by_request_size": None if traffic_exact is None else {
-            "bytes": traffic_exact,
-            "GBps": traffic_exact / (gather_ms / 1e3) / 1e9,
-            "note": "exact bytes leaving L2 from the request-size counters; roofline.traffic follows the FETCH_SIZE x "
-                    "copy-calibration method, which counts the 64-byte scale requests as 128 bytes",
+        "traffic_detail": None if traffic is None else {
+            "bytes_by_request_size": traffic,
+            "ratio_to_algorithmic": traffic / gather_bytes,
+            "GBps": traffic / (gather_ms / 1e3) / 1e9,
+            "fetch_size_estimate_bytes": traffic_fetch,
+            "note": "roofline.traffic: bytes leaving L2 per launch from the request-size counters (128-byte row "
+                    "reads, 64-byte scale reads, 64-byte writes); the FETCH_SIZE x copy-calibration estimate counts "
+                    "each 64-byte scale request as 128 bytes",
         },
+        "controls": controls,
+        "per_step_us": {"eager": ms_per_step * 1e3,
+                        "graph_two_call": None if graph is None else graph["two_call_us_per_step"],
+                        "graph_fused": None if graph is None else graph["fused_us_per_step"]},
         "gather_ms": gather_ms,
         "hash_ms": hash_ms,
         "us_per_step": ms_per_step * 1e3,

@@ -264,6 +264,17 @@ class Groups:
     n_unique: torch.Tensor
 
 
+def _check_groups(groups: Groups, n_tok: int) -> None:
+    """A Groups must be sized for exactly n_tok tokens: perm [n_tok], offsets [n_tok + 1], n_unique [>= 1]."""
+    if not isinstance(groups, Groups):
+        raise TypeError("groups must be a Groups")
+    for name, t, want in (("perm", groups.perm, n_tok), ("offsets", groups.offsets, n_tok + 1)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 1 or t.shape[0] != want:
+            raise ValueError(f"groups.{name} must be a 1-D tensor of {want} elements for {n_tok} tokens")
+    if not isinstance(groups.n_unique, torch.Tensor) or groups.n_unique.numel() < 1:
+        raise ValueError("groups.n_unique must hold at least one element")
+
+
 def gather_reduce(plan: Plan, addr: torch.Tensor, out: torch.Tensor | None = None, groups: Groups | None = None,
                   stream=None) -> torch.Tensor:
     """Per-module sum of the 24 dequantised rows: fp32 [n_tok, 2, 256] (engram_gather_reduce)."""
@@ -276,8 +287,7 @@ def gather_reduce(plan: Plan, addr: torch.Tensor, out: torch.Tensor | None = Non
         raise ValueError("out must be [n_tok, 2, 256]")
     perm = offsets = n_unique = None
     if groups is not None:
-        if groups.perm.shape[0] != n_tok or groups.offsets.shape[0] != n_tok + 1:
-            raise ValueError("groups do not match addr")
+        _check_groups(groups, n_tok)
         perm = _dev(groups.perm, torch.int32, "perm")
         offsets = _dev(groups.offsets, torch.int32, "offsets")
         n_unique = _dev(groups.n_unique, torch.int32, "n_unique")
@@ -370,6 +380,8 @@ def dedup(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, wo
         groups = Groups(torch.empty(n_tok, dtype=torch.int32, device=dev),
                         torch.empty(n_tok + 1, dtype=torch.int32, device=dev),
                         torch.empty(1, dtype=torch.int32, device=dev))
+    else:
+        _check_groups(groups, n_tok)
     need = dedup_workspace_bytes(n_tok)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

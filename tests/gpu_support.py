@@ -86,7 +86,8 @@ def sample_tokens(n_tok: int, k: int, seed: int, must=()) -> np.ndarray:
     pick.update(range(min(4, n_tok)))
     pick.add(n_tok - 1)
     if n_tok > k:
-        pick.update(rng.choice(n_tok, size=k - len(pick), replace=False).tolist())
+        while len(pick) < k:
+            pick.update(rng.choice(n_tok, size=k - len(pick), replace=False).tolist())
     else:
         pick.update(range(n_tok))
     return np.array(sorted(pick), dtype=np.int64)
@@ -117,3 +118,22 @@ def assert_within_tolerance(gpu: np.ndarray, ref: np.ndarray, abs_sum: np.ndarra
     if bad.any():
         i = np.flatnonzero(bad)[:5]
         raise AssertionError(f"{bad.sum()} elements out of tolerance; first: err={err[i]} bound={bound[i]}")
+
+
+def batch_sample(n_seq: int, seq_len: int, k: int, seed: int, seqs=(0, 1), positions=()) -> np.ndarray:
+    """``k`` token indices of an n_seq x seq_len batch (token = seq * seq_len + position), always including, for
+    every sequence in ``seqs``, positions 0-3, 63-65, the given ``positions`` and the last position, plus the
+    batch's first and last tokens; the rest uniform at random."""
+    must = []
+    for s in seqs:
+        if not 0 <= s < n_seq:
+            continue
+        for p in (0, 1, 2, 3, 63, 64, 65, seq_len - 1, *positions):
+            if 0 <= p < seq_len:
+                must.append(s * seq_len + p)
+    return sample_tokens(n_seq * seq_len, k, seed, must=must)
+
+
+def unwritten_tokens(out: torch.Tensor) -> int:
+    """Tokens of a NaN-initialised [n_tok, 2, 256] output whose first element of either module is still NaN."""
+    return int(torch.isnan(out[:, :, 0]).any(dim=1).sum().item())

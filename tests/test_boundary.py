@@ -310,3 +310,23 @@ def test_gather_reduce_batched_validation(hg, plan):
     assert L.engram_gather_reduce_batched(plan, None, 2, 3, FAKE, None) == EINVAL
     assert L.engram_gather_reduce_batched(plan, FAKE + 4, 2, 3, FAKE, None) == EINVAL
     assert L.engram_gather_reduce_batched(plan, FAKE, 2, 3, FAKE + 8, None) == EINVAL
+
+
+def test_binding_rejects_groups_of_another_size(hg):
+    """dedup() and gather_reduce() refuse a Groups sized for another token count before any call is made."""
+    import torch
+    ids = torch.zeros((2, 50), dtype=torch.int32)
+    addr = torch.zeros((100, 48), dtype=torch.int32).view(torch.uint32)
+    good = hg.Groups(torch.zeros(100, dtype=torch.int32), torch.zeros(101, dtype=torch.int32),
+                     torch.zeros(1, dtype=torch.int32))
+    bad = [
+        hg.Groups(torch.zeros(99, dtype=torch.int32), good.offsets, good.n_unique),
+        hg.Groups(good.perm, torch.zeros(100, dtype=torch.int32), good.n_unique),
+        hg.Groups(good.perm, good.offsets, torch.zeros(0, dtype=torch.int32)),
+        hg.Groups(torch.zeros((100, 1), dtype=torch.int32), good.offsets, good.n_unique),
+    ]
+    for g in bad:
+        with pytest.raises(ValueError, match="groups"):
+            hg.dedup(None, ids, groups=g)
+        with pytest.raises(ValueError, match="groups"):
+            hg.gather_reduce(None, addr, groups=g)

@@ -1,12 +1,15 @@
-"""engram_gather_reduce_batched: the direct-mode gather visiting a batch in tiles of positions gives the flat
-gather's result bitwise, for every shape (ragged last tiles, sequences shorter than a tile, one sequence, the
-2^24-item launch boundary) and both scale formats."""
+"""engram_gather_reduce_batched and the batched engram_lookup, which visit a batch in tiles of positions: against
+the oracle (full-size shared-prefix batch, a ragged batch, both sides of the 2^24-item launch split), and bitwise
+against the flat gather for every shape (ragged last tiles, sequences shorter than a tile, one sequence) and both
+scale formats."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
-from gpu_support import lib, small_device_tables, to_dev_ids
+from gpu_support import (addr_to_host, assert_within_tolerance, batch_sample, device_tables, lib, oracle_sampled,
+                         small_device_tables, to_dev_ids, unwritten_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,14 +43,66 @@ def test_batched_equals_flat(fmt, n_seq, seq_len, shared):
     assert torch.equal(fused, flat)
 
 
-def _token_checksums(out):
-    step = 1 << 20
-    return torch.cat([out[i:i + step].reshape(-1, 512).double().sum(dim=1) for i in range(0, out.shape[0], step)])
+def _batched_against_oracle(ids, hist, rows, seed, sample, what):
+    n_seq, seq_len = ids.shape
+    t, c = device_tables(rows, seed)
+    plan = lib().Plan(t, c)
+    d_ids, d_hist = to_dev_ids(ids, hist)
+    addr = lib().hash(plan, d_ids, d_hist)
+    out = torch.full((n_seq * seq_len, 2, 256), float("nan"), dtype=torch.float32, device="cuda")
+    lib().gather_reduce_batched(plan, addr, n_seq, out=out)
+    idx = torch.from_numpy(sample).cuda()
+    got = out[idx].cpu().numpy()
+    unwritten = unwritten_tokens(out)
+    got_addr = addr_to_host(addr)
+    out.fill_(float("nan"))
+    lib().lookup(plan, d_ids, d_hist, out=out)
+    got_fused = out[idx].cpu().numpy()
+    unwritten_fused = unwritten_tokens(out)
+    torch.cuda.synchronize()
+    del out, addr
+    torch.cuda.empty_cache()
+    assert unwritten == 0, f"{unwritten} tokens the batched gather never wrote"
+    assert unwritten_fused == 0, f"{unwritten_fused} tokens the fused lookup never wrote"
+    _say(f"oracle on {sample.size} sampled tokens ({what})")
+    want_addr, want, abs_sum = oracle_sampled(ids, hist, rows, seed, sample)
+    assert np.array_equal(got_addr, want_addr)
+    assert_within_tolerance(got, want, abs_sum)
+    assert_within_tolerance(got_fused, want, abs_sum)
+    assert np.array_equal(got_fused, got)
+
+
+def test_batched_shared_prefix_full_size_against_oracle():
+    """The shared-prefix batch (64 x (4,096 shared + 4,096 own), 48 x 2^24-row tables): the batch-order gather and
+    the batch-order fused lookup against the oracle on 8,192 sampled tokens, including positions 0-3, 63-65,
+    4,095-4,099 and the last one of several sequences."""
+    w = workloads.WORKLOADS[5]
+    _say(f"batched gather + fused lookup vs oracle, workload 5 n_tok={w.n_tok}")
+    ids, hist = workloads.make_ids(w)
+    sample = batch_sample(w.n_seq, w.seq_len, 8192, 55, seqs=(0, 1, 2, 31, 62, 63),
+                          positions=(127, 128, 4095, 4096, 4097, 4098, 4099, 8127, 8128))
+    _batched_against_oracle(ids, hist, w.rows, w.table_seed, sample, "workload 5")
+
+
+def test_batched_ragged_full_size_against_oracle():
+    """7 sequences of 4,133 positions (a 37-position last tile) sharing a 1,000-id prefix, on the full-size
+    tables: the batch-order paths against the oracle on 8,192 sampled tokens."""
+    w = workloads.WORKLOADS[5]
+    n_seq, seq_len, shared = 7, 4133, 1000
+    _say(f"batched gather + fused lookup vs oracle, {n_seq} x {seq_len}, ragged last tile")
+    rng = np.random.default_rng(4133)
+    ids = workloads.zipf_ids(rng, n_seq * seq_len).reshape(n_seq, seq_len)
+    ids[:, :shared] = ids[0, :shared]
+    sample = batch_sample(n_seq, seq_len, 8192, 56, seqs=tuple(range(n_seq)),
+                          positions=(999, 1000, 1001, 4095, 4096, 4097, 4131))
+    _batched_against_oracle(ids, None, w.rows, w.table_seed, sample, "ragged batch")
 
 
 def test_batched_across_the_chunk_boundary():
     """Two sequences of 2^23 + 40 tokens: the batched gather splits its grid at 2^24 items, where the last,
-    40-position tile begins; per-token checksums and a sample of tokens equal the flat gather's."""
+    40-position tile begins.  The output starts as NaN; tokens on both sides of the split (the last 1,200
+    positions of each sequence, the first 130, and 4,000 at random) are checked against the oracle and bitwise
+    against the flat gather, and no token is left unwritten."""
     n_seq, seq_len = 2, (1 << 23) + 40
     _say(f"batched gather, {n_seq} x {seq_len} tokens")
     R = 512
@@ -58,18 +113,25 @@ def test_batched_across_the_chunk_boundary():
     ids = rng.integers(0, 129280, size=(n_seq, seq_len), dtype=np.int64).astype(np.int32)
     d_ids, _ = to_dev_ids(ids, None)
     n_tok = n_seq * seq_len
-    sample = torch.from_numpy(np.unique(np.concatenate([
-        np.arange(0, 130), np.arange(seq_len - 100, seq_len + 100), np.arange(n_tok - 100, n_tok),
-        rng.integers(0, n_tok, 4000)]))).cuda()
+    sample = np.unique(np.concatenate([
+        np.arange(0, 130), np.arange(seq_len - 1200, seq_len + 130), np.arange(n_tok - 1200, n_tok),
+        rng.integers(0, n_tok, 4000)]))
+    idx = torch.from_numpy(sample).cuda()
     addr = lib().hash(plan, d_ids)
-    out = lib().gather_reduce_batched(plan, addr, n_seq)
-    batched_sum = _token_checksums(out)
-    batched_sample = out[sample].clone()
+    out = torch.full((n_tok, 2, 256), float("nan"), dtype=torch.float32, device="cuda")
+    lib().gather_reduce_batched(plan, addr, n_seq, out=out)
+    batched_sample = out[idx].cpu().numpy()
+    unwritten = unwritten_tokens(out)
+    out.fill_(float("nan"))
     lib().gather_reduce(plan, addr, out=out)
+    flat_sample = out[idx].cpu().numpy()
+    got_addr = addr.view(torch.int32)[idx].cpu().numpy().view(np.uint32)
     torch.cuda.synchronize()
-    flat_sum = _token_checksums(out)
-    flat_sample = out[sample].clone()
     del addr, out
     torch.cuda.empty_cache()
-    assert torch.equal(batched_sample, flat_sample)
-    assert torch.equal(batched_sum, flat_sum)
+    assert unwritten == 0
+    want_addr = oracle.hash_addresses(oracle.windows(ids)[sample], oracle.multipliers(), [R] * 48)
+    assert np.array_equal(got_addr, want_addr)
+    want, abs_sum = oracle.gather_reduce(host_t, host_c, want_addr)
+    assert_within_tolerance(batched_sample, want, abs_sum)
+    assert np.array_equal(batched_sample, flat_sample)

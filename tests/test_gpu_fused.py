@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_support import assert_within_tolerance, device_tables, lib, small_device_tables, to_dev_ids
+from gpu_support import assert_within_tolerance, device_tables, lib, small_device_tables, to_dev_ids, unwritten_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -103,7 +103,9 @@ def test_graph_replay_matches_eager():
 
 
 def test_launch_chunk_boundary():
-    """More than 2^24 tokens: the gather and the fused lookup split their grids at 2^24 items."""
+    """More than 2^24 tokens: the gather and the fused lookup split their grids at 2^24 items.  Each output starts
+    as NaN; 2,400 tokens on both sides of the split, the first and last tokens and 2,000 at random are checked
+    against the oracle, the fused result bitwise against the gather's, and no token may stay unwritten."""
     n_tok = (1 << 24) + 37
     _say(f"chunk boundary, {n_tok} tokens (3.2 GB addresses, 34 GB output)")
     R = 512
@@ -113,37 +115,37 @@ def test_launch_chunk_boundary():
     rng = np.random.default_rng(24)
     ids = rng.integers(0, 129280, size=(1, n_tok), dtype=np.int64).astype(np.int32)
     d_ids, _ = to_dev_ids(ids, None)
-    addr = lib().hash(plan, d_ids)
-    out = lib().gather_reduce(plan, addr)
-    torch.cuda.synchronize()
-    tokens = np.array([0, 1, 2, 3, (1 << 24) - 2, (1 << 24) - 1, 1 << 24, (1 << 24) + 1, n_tok - 2, n_tok - 1])
+    tokens = np.unique(np.concatenate([np.arange(0, 64), np.arange((1 << 24) - 2400, n_tok),
+                                       rng.integers(0, n_tok, 2000)]))
     idx = torch.from_numpy(tokens).cuda()
+    addr = lib().hash(plan, d_ids)
+    out = torch.full((n_tok, 2, 256), float("nan"), dtype=torch.float32, device="cuda")
+    lib().gather_reduce(plan, addr, out=out)
     got = out[idx].cpu().numpy()
+    unwritten = unwritten_tokens(out)
     got_addr = addr.view(torch.int32)[idx].cpu().numpy().view(np.uint32)
-    lookup_out = lib().lookup(plan, d_ids, out=out)  # reuse the buffer
+    out.fill_(float("nan"))
+    lib().lookup(plan, d_ids, out=out)
+    got_fused = out[idx].cpu().numpy()
+    unwritten_fused = unwritten_tokens(out)
     torch.cuda.synchronize()
-    got_fused = lookup_out[idx].cpu().numpy()
-    del addr, out, lookup_out
+    del addr, out
     torch.cuda.empty_cache()
+    assert unwritten == 0 and unwritten_fused == 0, (unwritten, unwritten_fused)
     win = oracle.windows(ids)[tokens]
     want_addr = oracle.hash_addresses(win, oracle.multipliers(), [R] * 48)
     assert np.array_equal(got_addr, want_addr)
     want, abs_sum = oracle.gather_reduce(host_t, host_c, want_addr)
     assert_within_tolerance(got, want, abs_sum)
+    assert_within_tolerance(got_fused, want, abs_sum)
     assert np.array_equal(got_fused, got)
-
-
-def _token_checksums(out):
-    """float64 sum of each token's 512 outputs, in chunks (no second full-size buffer)."""
-    step = 1 << 20
-    return torch.cat([out[i:i + step].reshape(-1, 512).double().sum(dim=1) for i in range(0, out.shape[0], step)])
 
 
 def test_batched_order_across_the_chunk_boundary():
     """Two sequences of 2^23 + 40 tokens: the fused lookup visits them in 64-position tiles and splits its grid at
-    2^24 items, which is where the last, 40-position tile begins.  Every token's output must be the two-call one:
-    both runs write one buffer in turn and their per-token checksums (deterministic sums of bitwise-equal data)
-    must agree exactly, and a sample of tokens is compared element by element."""
+    2^24 items, which is where the last, 40-position tile begins.  The output starts as NaN; the last 1,200
+    positions of each sequence (both sides of the split), the first 130 and 4,000 at random are checked against
+    the oracle and bitwise against the two-call path, and no token may stay unwritten."""
     n_seq, seq_len = 2, (1 << 23) + 40
     _say(f"fused batched order, {n_seq} x {seq_len} tokens")
     R = 512
@@ -154,21 +156,26 @@ def test_batched_order_across_the_chunk_boundary():
     ids = rng.integers(0, 129280, size=(n_seq, seq_len), dtype=np.int64).astype(np.int32)
     d_ids, _ = to_dev_ids(ids, None)
     n_tok = n_seq * seq_len
-    sample = torch.from_numpy(np.unique(np.concatenate([
-        np.arange(0, 130), np.arange(seq_len - 100, seq_len + 100), np.arange(n_tok - 100, n_tok),
-        rng.integers(0, n_tok, 4000)]))).cuda()
-    out = lib().lookup(plan, d_ids)
-    fused_sum = _token_checksums(out)
-    fused_sample = out[sample].clone()
+    sample = np.unique(np.concatenate([
+        np.arange(0, 130), np.arange(seq_len - 1200, seq_len + 130), np.arange(n_tok - 1200, n_tok),
+        rng.integers(0, n_tok, 4000)]))
+    idx = torch.from_numpy(sample).cuda()
+    out = torch.full((n_tok, 2, 256), float("nan"), dtype=torch.float32, device="cuda")
+    lib().lookup(plan, d_ids, out=out)
+    fused_sample = out[idx].cpu().numpy()
+    unwritten = unwritten_tokens(out)
     addr = lib().hash(plan, d_ids)
+    out.fill_(float("nan"))
     lib().gather_reduce(plan, addr, out=out)
+    two_sample = out[idx].cpu().numpy()
     torch.cuda.synchronize()
-    two_sum = _token_checksums(out)
-    two_sample = out[sample].clone()
     del addr, out
     torch.cuda.empty_cache()
-    assert torch.equal(fused_sample, two_sample)
-    assert torch.equal(fused_sum, two_sum)
+    assert unwritten == 0
+    want_addr = oracle.hash_addresses(oracle.windows(ids)[sample], oracle.multipliers(), [R] * 48)
+    want, abs_sum = oracle.gather_reduce(host_t, host_c, want_addr)
+    assert_within_tolerance(fused_sample, want, abs_sum)
+    assert np.array_equal(fused_sample, two_sample)
 
 
 def test_one_plan_on_two_streams():
