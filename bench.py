@@ -374,7 +374,7 @@ def main(argv=None) -> int:
         groups = hg.Groups(torch.empty(n_tok, dtype=torch.int32, device=dev),
                            torch.empty(n_tok + 1, dtype=torch.int32, device=dev),
                            torch.empty(1, dtype=torch.int32, device=dev))
-        ws = torch.empty(hg.dedup_workspace_bytes(n_tok), dtype=torch.uint8, device=dev)
+        ws = torch.empty(hg.dedup_workspace_bytes(plan, n_tok), dtype=torch.uint8, device=dev)
 
     def hash_phase(i):
         b = batches[i % len(batches)]

@@ -77,7 +77,7 @@ def _load():
         "engram_gather_reduce_batched": [P, VP, I64, I64, VP, VP],
         "engram_gather_weighted": [P, VP, I64, VP, VP, VP],
         "engram_gather_rows": [P, VP, I64, VP, VP],
-        "engram_dedup_workspace": [I64, ctypes.POINTER(ctypes.c_size_t)],
+        "engram_dedup_workspace": [P, I64, ctypes.POINTER(ctypes.c_size_t)],
         "engram_dedup": [P, VP, VP, I64, I64, VP, VP, VP, VP, ctypes.c_size_t, VP],
         "engram_synth_fill": [VP, VP, U64, U32, U64, VP],
         "engram_synth_fill_e8m0": [VP, U64, U32, U64, VP],
@@ -364,9 +364,10 @@ def gather_rows(plan: Plan, addr: torch.Tensor, out: torch.Tensor | None = None,
     return out
 
 
-def dedup_workspace_bytes(n_tok: int) -> int:
+def dedup_workspace_bytes(plan: Plan, n_tok: int) -> int:
+    """Workspace bytes of dedup for n_tok tokens under this plan (engram_dedup_workspace)."""
     b = ctypes.c_size_t()
-    _check(_lib.engram_dedup_workspace(n_tok, ctypes.byref(b)), "engram_dedup_workspace")
+    _check(_lib.engram_dedup_workspace(plan.handle, n_tok, ctypes.byref(b)), "engram_dedup_workspace")
     return b.value
 
 
@@ -382,7 +383,7 @@ def dedup(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, wo
                         torch.empty(1, dtype=torch.int32, device=dev))
     else:
         _check_groups(groups, n_tok)
-    need = dedup_workspace_bytes(n_tok)
+    need = dedup_workspace_bytes(plan, n_tok)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = _lib.engram_dedup(plan.handle, _dev(ids, torch.int32, "ids"),

@@ -8,31 +8,99 @@
 // Prompts that share a prefix repeat whole windows across sequences.
 //
 // Method: a stable least-significant-digit radix sort of (key, token) pairs
-// with 8-bit digits, then a group flag where the key changes, a scan of the
-// flags and the group start offsets.
+// with 8-bit digits, then group boundaries where the key changes.
 //
-// Key: with every id below 2^B (B from the plan's vocabulary bound, 31 when
-// none is given), the window packs exactly into 4B bits,
-//     key = w_0 * 2^(3B) + w_1 * 2^(2B) + w_2 * 2^B + w_3,
-// whose numeric order is the lexicographic order of (w_0, w_1, w_2, w_3).  A
-// 129,280-id vocabulary gives B = 17, a 68-bit key and 9 passes.
+// Key.  Each window id becomes a small integer m < 2^B and the window packs
+// into 4B bits, key = m_0 * 2^(3B) + m_1 * 2^(2B) + m_2 * 2^B + m_3, whose
+// numeric order is the lexicographic order of (w_0, w_1, w_2, w_3) as long
+// as id -> m is strictly increasing.  Two mappings:
+//   * compaction (vocabularies of 2^16 < V <= 2^18 ids): m is the rank of the
+//     id among the ids this call uses.  A presence map over the vocabulary,
+//     packed into a bitmap with prefix counts, gives the ranks, and B comes
+//     from their count D on
+//     the device: a 129,280-id vocabulary with 35,000 ids in use needs
+//     B = 16, a 64-bit key and 8 passes, instead of B = 17 (68 bits, 9
+//     passes).  The host launches the passes the vocabulary bound allows;
+//     the ones the device does not need return at once.
+//   * the id itself, B = ceil(log2 V) (31 when V is unknown), otherwise.
+// An id at or above V (a contract violation) gets m = D, or is masked to B
+// bits: its grouping is then unspecified, but nothing is read or written out
+// of bounds.
 //
-// A pass is three kernels, all with many blocks:
-//   hist:     per-block digit histogram (wave ballots group equal digits so a
-//             wave adds each distinct digit once)        -> cnt[digit][block]
-//   colscan:  one block per digit: exclusive scan over blocks -> cnt, and the
-//             digit's total                               -> tot[digit]
-//   scatter:  every block scans the 256 totals in LDS, then ranks its elements
-//             stably (per 256-element sub-tile: ballot match within a wave,
-//             per-wave counts in LDS across waves) and moves (key, token).
+// Presence map without clearing: an entry is "present" when it equals this
+// call's stamp, a counter kept in the workspace and advanced once per call.
+// A stale or uninitialised entry that happens to equal the stamp only adds a
+// rank nobody uses: ranks stay strictly increasing over the ids in use.
+//
+// One kernel per pass (onesweep): a tile of 8,192 elements ranks its
+// elements by digit (wave ballots, stable), publishes its per-digit counts,
+// and finds the counts of all earlier tiles by decoupled look-back: each
+// tile's status word per digit holds its count (state AGG) and, once known,
+// its inclusive prefix (state INC).  A wave reads the statuses of 64 earlier
+// tiles of one digit in one coalesced load (statuses are stored digit-major)
+// and sums back to the nearest INC, so a tile needs about T / 64 dependent
+// loads per digit, not T.  Tiles take their index from an atomic counter in
+// start order, so every tile waited on has started and publishes without
+// waiting on anyone: the waits end.  They are also bounded: past a spin
+// limit the tile records an error and stops waiting, every later wait and
+// pass gives up, and the group count comes out as -1.
+//
+// Kernels of one call, in stream order:
+//   init    clear counters, histograms and statuses; mark the ids in use
+//   bitmap  (compaction only) presence bitmap of the ids in use, with counts
+//   keys    build every key (ranks from the bitmap staged in LDS); B and the
+//           pass count; the histogram of the first pass's digit
+//   pass p  p = 0 .. passes the bound allows - 1; also counts the next
+//           pass's digit (the multiset of keys is the same in every pass);
+//           the last one needed writes the token order into the caller's perm
+//   groups  flags where the key changes, a look-back scan of their counts,
+//           offsets and the group count
+#include <algorithm>
+
 #include "engram_internal.h"
 
 namespace engram {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr uint32_t kTile = 1024;          // elements per block per pass (4 sub-tiles)
+constexpr uint32_t kRadix = 256;
+constexpr int kMaxPasses = 16;            // 4 x 31-bit ids = 124 key bits
+constexpr uint32_t kPassThreads = 1024;   // 16 waves
+constexpr uint32_t kPassWaves = kPassThreads / 64;
+constexpr uint32_t kItems = 4;            // elements per thread and tile
+constexpr uint32_t kTile = kPassThreads * kItems;  // 4,096 elements
+constexpr uint32_t kWaveSpan = 64 * kItems;        // elements per wave and tile
+constexpr uint32_t kKeyThreads = 512;
+constexpr uint32_t kKeyItems = 8;         // tokens per thread in the key kernel
+constexpr uint32_t kCompactMin = 1u << 16;  // compaction for vocabularies above this ...
+constexpr uint32_t kCompactMax = 1u << 18;  // ... up to this
+constexpr uint32_t kRankIds = 4096;        // ids per block of the presence bitmap (64 words)
+constexpr uint32_t kMaxBitmapBlocks = kCompactMax / kRankIds;  // 64
+constexpr uint32_t kSpinLimit = 1u << 18;  // waits of about 2^18 x 128 clocks (~14 ms) at most
+
+// Status words.  A pass tile publishes its 256 digit counts (each < 2^15)
+// as 128 words of two 16-bit halves, each half with its top bit set; a
+// group tile publishes one word, its count with the top bit set.  Zero means
+// "not published yet".
+constexpr uint32_t kPairReady = 0x80008000u;
+constexpr uint32_t kWordReady = 0x80000000u;
+constexpr uint32_t kStatusWords = kRadix / 2;  // words per pass tile
+constexpr uint32_t kGroupsOfRows = kPassThreads / kStatusWords;  // earlier tiles read in parallel per thread column
+
+// Control block at the start of the workspace.
+struct Ctl {
+    // written by init or rank, read by the later kernels of the call
+    uint32_t stamp;     // presence stamp of the last call (kept across calls)
+    uint32_t npass;     // passes this call needs
+    uint32_t has_hi;    // keys wider than 64 bits
+    uint32_t bits;      // B
+    uint32_t n_ids;     // D (compaction) or 0
+    uint32_t pad0[59];
+    // modified with atomics during the call
+    uint32_t tile_ctr[kMaxPasses + 1];  // tile tickets of each pass, and of the group kernel
+    uint32_t error;                     // a look-back gave up
+    uint32_t pad1[46];
+};
+static_assert(sizeof(Ctl) == 512, "control block size");
 
 struct Ids {
     const int32_t* ids;
@@ -49,23 +117,53 @@ __device__ __forceinline__ uint32_t window_word(const Ids& s, uint32_t tok, int 
     return 0u;
 }
 
-__global__ __launch_bounds__(kThreads) void build_keys_kernel(Ids s, uint32_t n, uint32_t bits,
-                                                              uint64_t* __restrict__ klo, uint64_t* __restrict__ khi,
-                                                              int32_t* __restrict__ val) {
-    const uint32_t tok = blockIdx.x * kThreads + threadIdx.x;
-    if (tok >= n) return;
-    uint64_t lo = 0, hi = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {  // w_0 most significant
-        hi = (hi << bits) | (lo >> (64 - bits));
-        lo = (lo << bits) | window_word(s, tok, k);
-    }
-    klo[tok] = lo;
-    khi[tok] = hi;
-    val[tok] = static_cast<int32_t>(tok);
+__device__ __forceinline__ uint32_t load_status(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_status(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Lanes of this wave whose `valid` digit equals this lane's.
+// Inclusive scan over the 64 lanes with DPP moves: row_shr 1, 2, 4, 8 within
+// each row of 16 lanes, then row_bcast 15 and 31 across rows.  Plain VALU
+// operations, with no LDS round trip (unlike a shuffle).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1 and 3
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Sum over the 64 lanes, returned to every lane.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+    return __builtin_amdgcn_readlane(wave_inclusive_scan(x), 63);
+}
+
+__host__ __device__ inline uint32_t bits_for(uint64_t count) {  // smallest B >= 1 with 2^B >= count
+    uint32_t b = 1;
+    while (b < 31 && (uint64_t(1) << b) < count) ++b;
+    return b;
+}
+
+// Wait until a published status word is ready; bounded.  Returns the word,
+// or 0 after recording an error when the wait gives up.
+__device__ __forceinline__ uint32_t wait_ready(const uint32_t* p, uint32_t word, uint32_t ready, uint32_t* error) {
+    uint32_t spins = 0;
+    while ((word & ready) != ready) {
+        if (++spins > kSpinLimit || load_status(error) != 0u) {
+            store_status(error, 1u);
+            return 0u;
+        }
+        __builtin_amdgcn_s_sleep(8);
+        word = load_status(p);
+    }
+    return word;
+}
+
+// Lanes of this wave whose digit equals this lane's (valid lanes only).
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
     uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -77,199 +175,506 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool valid) {
     return peers;
 }
 
-__global__ __launch_bounds__(kThreads) void hist_kernel(const uint64_t* __restrict__ klo,
-                                                        const uint64_t* __restrict__ khi, uint32_t n, int pass,
-                                                        uint32_t* __restrict__ cnt) {
-    __shared__ uint32_t h[256];
-    h[threadIdx.x] = 0;
-    __syncthreads();
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint64_t lt = (uint64_t(1) << lane) - 1u;
-    const uint64_t* key = pass < 8 ? klo : khi;
-    const int sh = 8 * (pass & 7);
-    const uint32_t begin = blockIdx.x * kTile;
-#pragma unroll
-    for (uint32_t j = 0; j < kTile / kThreads; ++j) {
-        const uint32_t i = begin + j * kThreads + threadIdx.x;
-        const bool valid = i < n;
-        const uint32_t d = valid ? static_cast<uint32_t>(key[i] >> sh) & 0xFFu : 0u;
-        const uint64_t peers = match_digit(d, valid);
-        if (valid && (peers & lt) == 0) atomicAdd(&h[d], static_cast<uint32_t>(__popcll(peers)));
-    }
-    __syncthreads();
-    cnt[static_cast<size_t>(threadIdx.x) * gridDim.x + blockIdx.x] = h[threadIdx.x];
+__device__ __forceinline__ uint32_t key_digit(uint64_t lo, uint64_t hi, int pass) {
+    return static_cast<uint32_t>((pass < 8 ? lo >> (8 * pass) : hi >> (8 * (pass - 8)))) & 0xFFu;
 }
 
-// Block-wide exclusive scan of one value per thread (blockDim.x = 1024).
-__device__ __forceinline__ uint32_t block_exclusive_scan_1024(uint32_t x, uint32_t* part, uint32_t* total) {
-    part[threadIdx.x] = x;
-    __syncthreads();
-    for (uint32_t off = 1; off < 1024u; off <<= 1) {
-        const uint32_t add = threadIdx.x >= off ? part[threadIdx.x - off] : 0u;
-        __syncthreads();
-        part[threadIdx.x] += add;
-        __syncthreads();
+struct Workspace {
+    Ctl* ctl;
+    uint32_t* hist;    // [kMaxPasses][256] digit totals
+    uint32_t* status;  // [passes][tiles][128] digit counts of each pass tile, then [tiles] group counts
+    uint32_t* flags;   // [V] presence stamps (compaction)
+    uint64_t* bitmap;  // [64 * blocks] ids in use, one bit each (compaction)
+    uint32_t* wpre;    // [64 * blocks] ids in use below each bitmap word, within its block of 4,096 ids
+    uint32_t* bcount;  // [blocks] ids in use per block of 4,096 ids
+    uint64_t* lo[2];   // [n] key bits 0..63
+    uint64_t* hi[2];   // [n] key bits 64..127 (when the bound allows them)
+    int32_t* val[2];   // [n] token indices between passes
+};
+
+// How a call keys its windows, from host-side facts alone.
+struct KeyPlan {
+    bool compact;
+    uint32_t bits;     // B for id keys; the bound on B with compaction
+    int max_passes;    // passes launched
+    bool hi_possible;  // keys may exceed 64 bits
+};
+
+KeyPlan key_plan(uint32_t vocab) {
+    KeyPlan k;
+    k.compact = vocab > kCompactMin && vocab <= kCompactMax;
+    if (k.compact) {
+        // D <= V (a stale presence entry can count an id the call does not use); one more rank marks ids out
+        // of range
+        k.bits = bits_for(uint64_t(vocab) + 1u);
+    } else {
+        k.bits = vocab == 0 ? 31u : bits_for(vocab);
     }
-    const uint32_t incl = part[threadIdx.x];
-    if (total) *total = part[1023];
-    return incl - x;
+    k.max_passes = static_cast<int>((4 * k.bits + 7) / 8);
+    k.hi_possible = 4 * k.bits > 64;
+    return k;
 }
 
-// One block (1024 threads) per digit: exclusive scan of cnt[digit][0..blocks).
-__global__ __launch_bounds__(1024) void colscan_kernel(uint32_t* __restrict__ cnt, uint32_t blocks,
-                                                       uint32_t* __restrict__ tot) {
-    __shared__ uint32_t part[1024];
-    __shared__ uint32_t total;
-    uint32_t* row = cnt + static_cast<size_t>(blockIdx.x) * blocks;
-    const uint32_t per = (blocks + 1023u) / 1024u;
-    const uint32_t b0 = min(blocks, threadIdx.x * per), b1 = min(blocks, b0 + per);
-    uint32_t sum = 0;
-    for (uint32_t b = b0; b < b1; ++b) sum += row[b];
-    uint32_t run = block_exclusive_scan_1024(sum, part, &total);
-    for (uint32_t b = b0; b < b1; ++b) {
-        const uint32_t x = row[b];
-        row[b] = run;
-        run += x;
+size_t align_up(size_t x) { return (x + 255u) & ~size_t(255u); }
+
+size_t status_words(const KeyPlan& k, uint32_t tiles) { return (size_t(k.max_passes) * kStatusWords + 1) * tiles; }
+
+size_t layout(uint32_t n, uint32_t vocab, char* base, Workspace* w) {
+    const KeyPlan k = key_plan(vocab);
+    const uint32_t tiles = (n + kTile - 1u) / kTile;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off += align_up(bytes);
+        return p;
+    };
+    Workspace t{};
+    t.ctl = reinterpret_cast<Ctl*>(take(sizeof(Ctl)));
+    t.hist = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * kMaxPasses * kRadix));
+    t.status = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * status_words(k, tiles)));
+    if (k.compact) {
+        const uint32_t blocks = (vocab + kRankIds - 1u) / kRankIds;
+        t.flags = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * vocab));
+        t.bitmap = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * 64u * blocks));
+        t.wpre = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 64u * blocks));
+        t.bcount = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * blocks));
     }
-    if (threadIdx.x == 0) tot[blockIdx.x] = total;
+    for (int i = 0; i < 2; ++i) t.lo[i] = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * n));
+    if (k.hi_possible)
+        for (int i = 0; i < 2; ++i) t.hi[i] = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * n));
+    for (int i = 0; i < 2; ++i) t.val[i] = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * n));
+    if (w) *w = t;
+    return off;
 }
 
-__global__ __launch_bounds__(kThreads) void scatter_kernel(const uint64_t* __restrict__ klo,
-                                                           const uint64_t* __restrict__ khi,
-                                                           const int32_t* __restrict__ val, uint32_t n, int pass,
-                                                           const uint32_t* __restrict__ cnt,
-                                                           const uint32_t* __restrict__ tot,
-                                                           uint64_t* __restrict__ klo_out,
-                                                           uint64_t* __restrict__ khi_out,
-                                                           int32_t* __restrict__ val_out) {
-    __shared__ uint32_t base[256];  // next output slot of each digit for this block
-    __shared__ uint32_t wave_cnt[kWaves][256];
-    __shared__ uint32_t wsum[kWaves];
+// ---------------------------------------------------------------------------
+// init: clear the per-call state; mark the ids in use (compaction)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void init_kernel(Ids s, uint32_t n, uint32_t vocab, uint32_t compact,
+                                                   uint32_t zero_words, Workspace w, uint32_t id_bits,
+                                                   uint32_t id_passes, uint32_t id_hi) {
+    const uint32_t gtid = blockIdx.x * 256u + threadIdx.x;
+    const uint32_t stride = gridDim.x * 256u;
+    if (gtid <= kMaxPasses) w.ctl->tile_ctr[gtid] = 0u;
+    if (gtid == 0) w.ctl->error = 0u;
+    for (uint32_t i = gtid; i < zero_words; i += stride) w.hist[i] = 0u;  // histograms and statuses
+    if (gtid == 0 && !compact) {
+        w.ctl->bits = id_bits;
+        w.ctl->npass = id_passes;
+        w.ctl->has_hi = id_hi;
+        w.ctl->n_ids = 0;
+    }
+    if (!compact) return;
+    const uint32_t stamp = w.ctl->stamp + 1u;
+    for (uint32_t tok = gtid; tok < n; tok += stride) {
+        const uint32_t id = static_cast<uint32_t>(s.ids[tok]);
+        if (id < vocab) w.flags[id] = stamp;
+        const uint32_t seq = tok / s.seq_len;
+        if (tok == seq * s.seq_len) {  // first token of a sequence: the ids before it
+            for (uint32_t k = 0; k < 3; ++k) {
+                const uint32_t h = s.history ? static_cast<uint32_t>(s.history[seq * 3u + k]) : 0u;
+                if (h < vocab) w.flags[h] = stamp;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bitmap (compaction): block b turns the presence stamps of ids
+// [4096 b, 4096 (b+1)) into 64 bitmap words, the count of ids in use below
+// each word within the block, and the block's count
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bitmap_kernel(uint32_t vocab, Workspace w) {
+    __shared__ uint32_t wcnt[64];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
-    const uint64_t lt = (uint64_t(1) << lane) - 1u;
-
-    // Exclusive scan of the 256 digit totals (4 waves x 64 lanes).
-    {
-        const uint32_t t = tot[threadIdx.x];
-        uint32_t x = t;
+    const uint32_t stamp = w.ctl->stamp + 1u;
+    const uint32_t word0 = blockIdx.x * 64u + wave * 16u;  // this wave's 16 words
+    uint64_t word[16];
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_up(x, off);
-            if (lane >= static_cast<uint32_t>(off)) x += y;
-        }
-        if (lane == 63) wsum[wave] = x;
-        __syncthreads();
+    for (uint32_t c = 0; c < 16; ++c) {
+        const uint32_t id = ((word0 + c) << 6) + lane;
+        word[c] = __ballot(id < vocab && w.flags[id] == stamp);
+    }
+    uint64_t mine = 0;
+#pragma unroll
+    for (uint32_t c = 0; c < 16; ++c)
+        if (lane == c) mine = word[c];
+    if (lane < 16) {
+        w.bitmap[word0 + lane] = mine;
+        wcnt[wave * 16u + lane] = static_cast<uint32_t>(__popcll(mine));
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
         uint32_t pre = 0;
-        for (uint32_t w = 0; w < wave; ++w) pre += wsum[w];
-        base[threadIdx.x] = pre + x - t + cnt[static_cast<size_t>(threadIdx.x) * gridDim.x + blockIdx.x];
+        for (uint32_t c = 0; c < threadIdx.x; ++c) pre += wcnt[c];
+        w.wpre[blockIdx.x * 64u + threadIdx.x] = pre;
+        if (threadIdx.x == 63) w.bcount[blockIdx.x] = pre + wcnt[63];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// keys: pack every window; digit histograms of the passes this call needs.
+// A block stages its 4,096 ids (and the 3 before them) and, with compaction,
+// the whole presence bitmap with its prefix counts in LDS, so a key costs no
+// dependent global loads: rank(id) = ids in use in earlier 4,096-id blocks +
+// ids in use earlier in the block's words + set bits below id in its word.
+// With compaction the first block also records B, the pass count and the
+// stamp for the rest of the call.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kKeyThreads) void keys_kernel(Ids s, uint32_t n, uint32_t vocab, uint32_t compact,
+                                                           Workspace w) {
+    constexpr uint32_t kKeyTile = kKeyThreads * kKeyItems;
+    constexpr uint32_t kStage = (kKeyTile + 3u + kKeyThreads - 1u) / kKeyThreads;  // staged ids per thread
+    constexpr uint32_t kWordsPerThread = 64u * kMaxBitmapBlocks / kKeyThreads;
+    constexpr uint32_t kKeyWaves = kKeyThreads / 64;
+    __shared__ int32_t ids_s[kKeyTile + 3];
+    __shared__ uint64_t bits_s[64 * kMaxBitmapBlocks];
+    __shared__ uint32_t wpre_s[64 * kMaxBitmapBlocks];
+    __shared__ uint32_t bpre_s[kMaxBitmapBlocks];
+    __shared__ uint32_t h[kKeyWaves][kRadix];
+    __shared__ uint32_t s_d;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t begin = blockIdx.x * kKeyTile;
+    {  // the block's ids and the 3 before them; every load issued before the first store
+        int32_t v[kStage];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) wave_cnt[w][threadIdx.x] = 0;
+        for (uint32_t c = 0; c < kStage; ++c) {
+            const uint32_t i = c * kKeyThreads + threadIdx.x;
+            const int64_t tok = int64_t(begin) + int64_t(i) - 3;
+            v[c] = (i < kKeyTile + 3u && tok >= 0 && tok < int64_t(n)) ? s.ids[tok] : 0;
+        }
+#pragma unroll
+        for (uint32_t c = 0; c < kStage; ++c) {
+            const uint32_t i = c * kKeyThreads + threadIdx.x;
+            if (i < kKeyTile + 3u) ids_s[i] = v[c];
+        }
+    }
+    for (uint32_t i = threadIdx.x; i < kKeyWaves * kRadix; i += kKeyThreads) (&h[0][0])[i] = 0u;
+    uint32_t b, has_hi, n_ids = 0;
+    if (compact) {
+        const uint32_t blocks = (vocab + kRankIds - 1u) / kRankIds;
+        const uint32_t words = 64u * blocks;
+        uint64_t bw[kWordsPerThread];
+        uint32_t pw[kWordsPerThread];
+#pragma unroll
+        for (uint32_t c = 0; c < kWordsPerThread; ++c) {
+            const uint32_t i = c * kKeyThreads + threadIdx.x;
+            bw[c] = i < words ? w.bitmap[i] : 0u;
+            pw[c] = i < words ? w.wpre[i] : 0u;
+        }
+        const uint32_t bc = threadIdx.x < blocks ? w.bcount[threadIdx.x] : 0u;
+#pragma unroll
+        for (uint32_t c = 0; c < kWordsPerThread; ++c) {
+            const uint32_t i = c * kKeyThreads + threadIdx.x;
+            if (i < words) {
+                bits_s[i] = bw[c];
+                wpre_s[i] = pw[c];
+            }
+        }
+        if (threadIdx.x < kMaxBitmapBlocks) bpre_s[threadIdx.x] = bc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t run = 0;
+            for (uint32_t i = 0; i < blocks; ++i) {
+                const uint32_t c = bpre_s[i];
+                bpre_s[i] = run;
+                run += c;
+            }
+            s_d = run;
+        }
+        __syncthreads();
+        n_ids = s_d;
+        b = bits_for(uint64_t(n_ids) + 1u);
+        has_hi = 4u * b > 64u ? 1u : 0u;
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            w.ctl->n_ids = n_ids;
+            w.ctl->bits = b;
+            w.ctl->npass = (4u * b + 7u) / 8u;
+            w.ctl->has_hi = has_hi;
+            w.ctl->stamp = w.ctl->stamp + 1u;  // the presence stamps of this call are consumed
+        }
+    } else {
+        b = w.ctl->bits;
+        has_hi = w.ctl->has_hi;
         __syncthreads();
     }
-
-    const uint32_t begin = blockIdx.x * kTile;
-    const int sh = 8 * (pass & 7);
-    for (uint32_t j = 0; j < kTile / kThreads; ++j) {
-        const uint32_t i = begin + j * kThreads + threadIdx.x;
-        const bool valid = i < n;
+    const uint32_t mask = (1u << b) - 1u;
+    for (uint32_t j = 0; j < kKeyItems; ++j) {
+        const uint32_t tok = begin + j * kKeyThreads + threadIdx.x;
+        const bool valid = tok < n;
         uint64_t lo = 0, hi = 0;
-        int32_t v = 0;
         if (valid) {
-            lo = klo[i];
-            hi = khi[i];
-            v = val[i];
-        }
-        const uint32_t d = static_cast<uint32_t>((pass < 8 ? lo : hi) >> sh) & 0xFFu;
-        const uint64_t peers = match_digit(d, valid);
-        const uint32_t rank_in_wave = __popcll(peers & lt);
-        if (valid && rank_in_wave == 0) wave_cnt[wave][d] = __popcll(peers);
-        __syncthreads();
-        if (valid) {
-            uint32_t pos = base[d] + rank_in_wave;
-            for (uint32_t w = 0; w < wave; ++w) pos += wave_cnt[w][d];
-            klo_out[pos] = lo;
-            khi_out[pos] = hi;
-            val_out[pos] = v;
-        }
-        __syncthreads();
-        uint32_t add = 0;
+            const uint32_t seq = tok / s.seq_len;
+            const int32_t t = static_cast<int32_t>(tok - seq * s.seq_len);
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            add += wave_cnt[w][threadIdx.x];
-            wave_cnt[w][threadIdx.x] = 0;
+            for (int k = 0; k < 4; ++k) {  // w_0 most significant
+                uint32_t id;
+                if (t - k >= 0)
+                    id = static_cast<uint32_t>(ids_s[tok - begin + 3u - static_cast<uint32_t>(k)]);
+                else
+                    id = s.history ? static_cast<uint32_t>(s.history[seq * 3u + static_cast<uint32_t>(3 + t - k)]) : 0u;
+                uint32_t m;
+                if (compact) {
+                    m = n_ids;  // ids out of range share the rank after the last
+                    if (id < vocab) {
+                        const uint32_t wd = id >> 6;
+                        m = bpre_s[id >> 12] + wpre_s[wd] +
+                            static_cast<uint32_t>(__popcll(bits_s[wd] & ((uint64_t(1) << (id & 63u)) - 1u)));
+                    }
+                } else {
+                    m = id & mask;
+                }
+                hi = (hi << b) | (lo >> (64u - b));
+                lo = (lo << b) | m;
+            }
+            w.lo[0][tok] = lo;
+            if (has_hi) w.hi[0][tok] = hi;
         }
-        base[threadIdx.x] += add;
-        __syncthreads();
+        // histogram of the first pass's digit (each later pass counts its successor's)
+        if (valid) atomicAdd(&h[wave][static_cast<uint32_t>(lo) & 0xFFu], 1u);
     }
-}
-
-__device__ __forceinline__ uint32_t group_flag(const uint64_t* __restrict__ klo, const uint64_t* __restrict__ khi,
-                                               uint32_t i) {
-    return (i == 0 || klo[i] != klo[i - 1] || khi[i] != khi[i - 1]) ? 1u : 0u;
-}
-
-__global__ __launch_bounds__(kThreads) void flag_count_kernel(const uint64_t* __restrict__ klo,
-                                                              const uint64_t* __restrict__ khi, uint32_t n,
-                                                              uint32_t* __restrict__ bsum) {
-    const uint32_t begin = blockIdx.x * kTile;
-    uint32_t local = 0;
-    for (uint32_t i = begin + threadIdx.x; i < min(n, begin + kTile); i += kThreads) local += group_flag(klo, khi, i);
-    __shared__ uint32_t c[kWaves];
-    // wave reduction
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
-    if ((threadIdx.x & 63u) == 0) c[threadIdx.x >> 6] = local;
     __syncthreads();
-    if (threadIdx.x == 0) bsum[blockIdx.x] = c[0] + c[1] + c[2] + c[3];
-}
-
-// Exclusive scan of len values with one block of 1024 threads; total to *total.
-__global__ __launch_bounds__(1024) void scan_kernel(uint32_t* __restrict__ v, uint32_t len,
-                                                    uint32_t* __restrict__ total) {
-    __shared__ uint32_t part[1024];
-    const uint32_t per = (len + 1023u) / 1024u;
-    const uint32_t b0 = min(len, threadIdx.x * per), b1 = min(len, b0 + per);
-    uint32_t sum = 0;
-    for (uint32_t i = b0; i < b1; ++i) sum += v[i];
-    uint32_t run = block_exclusive_scan_1024(sum, part, total);
-    for (uint32_t i = b0; i < b1; ++i) {
-        const uint32_t x = v[i];
-        v[i] = run;
-        run += x;
+    if (threadIdx.x < kRadix) {
+        uint32_t c = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kKeyWaves; ++k) c += h[k][threadIdx.x];
+        if (c) atomicAdd(&w.hist[threadIdx.x], c);
     }
 }
 
-__global__ __launch_bounds__(kThreads) void group_offsets_kernel(const uint64_t* __restrict__ klo,
-                                                                 const uint64_t* __restrict__ khi, uint32_t n,
-                                                                 const uint32_t* __restrict__ bsum,
-                                                                 const uint32_t* __restrict__ total,
-                                                                 int32_t* __restrict__ offsets,
-                                                                 int32_t* __restrict__ n_unique) {
-    __shared__ uint32_t wave_sum[kWaves];
-    __shared__ uint32_t run;
+// ---------------------------------------------------------------------------
+// one pass of the radix sort: rank, look back, scatter
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass, uint32_t tiles, Workspace w,
+                                                            int32_t* __restrict__ perm) {
+    Ctl* ctl = w.ctl;
+    const uint32_t npass = ctl->npass;
+    if (static_cast<uint32_t>(pass) >= npass) return;  // this call's keys need fewer passes
+    const bool has_hi = ctl->has_hi != 0u;
+    const bool last = static_cast<uint32_t>(pass) + 1u == npass;
+
+    __shared__ uint32_t s_tile;
+    __shared__ uint32_t wave_hist[kPassWaves][kRadix];  // counts per wave, then exclusive prefixes across waves
+    __shared__ uint32_t next_hist[kPassWaves][kRadix];  // this tile's counts of the next pass's digit, per wave
+    __shared__ uint32_t tile_cnt[kRadix];
+    __shared__ uint32_t base[kRadix];  // where the tile's run of each digit starts in the output
+    __shared__ uint32_t wsum[kRadix / 64];
+    __shared__ uint32_t part[2][kGroupsOfRows][kStatusWords];  // earlier tiles' counts, per row group
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
     const uint64_t lt = (uint64_t(1) << lane) - 1u;
-    if (threadIdx.x == 0) run = bsum[blockIdx.x];
-    __syncthreads();
-    const uint32_t begin = blockIdx.x * kTile;
-    for (uint32_t j = 0; j < kTile / kThreads; ++j) {
-        const uint32_t i = begin + j * kThreads + threadIdx.x;
-        const uint32_t f = i < n ? group_flag(klo, khi, i) : 0u;
-        const uint64_t m = __ballot(f);
-        if (lane == 0) wave_sum[wave] = __popcll(m);
-        __syncthreads();
-        uint32_t pos = run + __popcll(m & lt);
-        for (uint32_t w = 0; w < wave; ++w) pos += wave_sum[w];
-        if (f) offsets[pos] = static_cast<int32_t>(i);
-        __syncthreads();
-        if (threadIdx.x == 0) run += wave_sum[0] + wave_sum[1] + wave_sum[2] + wave_sum[3];
-        __syncthreads();
+    uint32_t total = 0;  // this pass's total count of digit threadIdx.x (threads 0..255)
+    if (threadIdx.x < kRadix) total = w.hist[pass * kRadix + threadIdx.x];
+    if (threadIdx.x == 0) s_tile = atomicAdd(&ctl->tile_ctr[pass], 1u);
+    for (uint32_t i = threadIdx.x; i < kPassWaves * kRadix; i += kPassThreads) {
+        (&wave_hist[0][0])[i] = 0u;
+        (&next_hist[0][0])[i] = 0u;
     }
-    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
-        offsets[*total] = static_cast<int32_t>(n);
-        *n_unique = static_cast<int32_t>(*total);
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    const int src = pass & 1, dst = src ^ 1;
+    const uint64_t* __restrict__ lo_in = w.lo[src];
+    const uint64_t* __restrict__ hi_in = w.hi[src];
+    const int32_t* __restrict__ val_in = w.val[src];
+    uint64_t* __restrict__ lo_out = w.lo[dst];
+    uint64_t* __restrict__ hi_out = w.hi[dst];
+    int32_t* __restrict__ val_out = last ? perm : w.val[dst];
+
+    // this wave's 1,024 elements, 64 consecutive per step (steps in element order: the ranking is stable)
+    const uint32_t first = tile * kTile + wave * kWaveSpan;
+    uint64_t lo[kItems], hi[kItems];
+    int32_t v[kItems];
+#pragma unroll
+    for (uint32_t j = 0; j < kItems; ++j) {
+        const uint32_t i = first + j * 64u + lane;
+        const bool valid = i < n;
+        lo[j] = valid ? lo_in[i] : 0u;
+        hi[j] = (valid && has_hi) ? hi_in[i] : 0u;
+        v[j] = valid ? (pass == 0 ? static_cast<int32_t>(i) : val_in[i]) : 0;
+    }
+    uint32_t off[kItems];
+#pragma unroll
+    for (uint32_t j = 0; j < kItems; ++j) {
+        const bool valid = first + j * 64u + lane < n;
+        const uint32_t d = key_digit(lo[j], hi[j], pass);
+        const uint64_t peers = match_digit(d, valid);
+        const uint32_t before = wave_hist[wave][d];
+        off[j] = before + static_cast<uint32_t>(__popcll(peers & lt));
+        if (valid && (peers & lt) == 0) wave_hist[wave][d] = before + static_cast<uint32_t>(__popcll(peers));
+    }
+    __syncthreads();
+
+    if (threadIdx.x < kRadix) {
+        const uint32_t dd = threadIdx.x;
+        uint32_t run = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kPassWaves; ++k) {
+            const uint32_t c = wave_hist[k][dd];
+            wave_hist[k][dd] = run;
+            run += c;
+        }
+        tile_cnt[dd] = run;
+        // exclusive scan of the pass's digit totals (threads 0..255 are waves 0..3)
+        const uint32_t x = wave_inclusive_scan(total);
+        if (lane == 63) wsum[wave] = x;
+        base[dd] = x - total;
+    }
+    __syncthreads();
+    // publish this tile's counts: word i holds digits 2i (low half) and 2i + 1 (high half)
+    const uint32_t* counts = w.status + size_t(pass) * tiles * kStatusWords;  // [tiles][128]
+    if (threadIdx.x < kStatusWords) {
+        const uint32_t i = threadIdx.x;
+        store_status(w.status + (size_t(pass) * tiles + tile) * kStatusWords + i,
+                     kPairReady | tile_cnt[2 * i] | (tile_cnt[2 * i + 1] << 16));
+    }
+    if (threadIdx.x < kRadix) {
+        uint32_t pre = 0;
+        for (uint32_t k = 0; k < wave; ++k) pre += wsum[k];
+        base[threadIdx.x] += pre;
+    }
+    {  // counts in the earlier tiles: thread (g, i) sums word i of tiles g, g + 8, g + 16, ... below this one
+        const uint32_t g = threadIdx.x / kStatusWords, i = threadIdx.x % kStatusWords;
+        uint32_t sum_lo = 0, sum_hi = 0;
+        bool counted = last;  // this thread's items are in the next digit's counts (none needed after the last pass)
+        for (uint32_t t0 = g; t0 < tile; t0 += 8u * kGroupsOfRows) {
+            uint32_t v[8];
+#pragma unroll
+            for (uint32_t j = 0; j < 8; ++j) {
+                const uint32_t t = t0 + j * kGroupsOfRows;
+                v[j] = t < tile ? load_status(counts + size_t(t) * kStatusWords + i) : kPairReady;
+            }
+            if (!counted) {  // while the first loads are in flight: this tile's counts of the next digit
+#pragma unroll
+                for (uint32_t j = 0; j < kItems; ++j)
+                    if (first + j * 64u + lane < n) atomicAdd(&next_hist[wave][key_digit(lo[j], hi[j], pass + 1)], 1u);
+                counted = true;
+            }
+#pragma unroll
+            for (uint32_t j = 0; j < 8; ++j) {
+                const uint32_t t = t0 + j * kGroupsOfRows;
+                if (t < tile) {
+                    const uint32_t c = wait_ready(counts + size_t(t) * kStatusWords + i, v[j], kPairReady, &ctl->error);
+                    sum_lo += c & 0x7FFFu;
+                    sum_hi += (c >> 16) & 0x7FFFu;
+                }
+            }
+        }
+        if (!counted) {  // no earlier tile for this thread to read
+#pragma unroll
+            for (uint32_t j = 0; j < kItems; ++j)
+                if (first + j * 64u + lane < n) atomicAdd(&next_hist[wave][key_digit(lo[j], hi[j], pass + 1)], 1u);
+        }
+        part[0][g][i] = sum_lo;
+        part[1][g][i] = sum_hi;
+    }
+    __syncthreads();
+    if (threadIdx.x < kRadix) {
+        const uint32_t dd = threadIdx.x;
+        uint32_t e = 0;
+#pragma unroll
+        for (uint32_t g = 0; g < kGroupsOfRows; ++g) e += part[dd & 1u][g][dd >> 1];
+        base[dd] += e;
+        if (!last) {
+            uint32_t c = 0;
+#pragma unroll
+            for (uint32_t k = 0; k < kPassWaves; ++k) c += next_hist[k][dd];
+            if (c) atomicAdd(&w.hist[(pass + 1) * kRadix + dd], c);
+        }
+    }
+    __syncthreads();
+    if (load_status(&ctl->error) != 0u) return;  // a wait gave up somewhere: the positions are not to be trusted
+
+#pragma unroll
+    for (uint32_t j = 0; j < kItems; ++j) {
+        const uint32_t i = first + j * 64u + lane;
+        if (i < n) {
+            const uint32_t d = key_digit(lo[j], hi[j], pass);
+            const uint32_t pos = base[d] + wave_hist[wave][d] + off[j];
+            if (pos < n) {
+                lo_out[pos] = lo[j];
+                if (has_hi) hi_out[pos] = hi[j];
+                val_out[pos] = v[j];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// groups: boundaries where the sorted key changes -> offsets, n_unique
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kPassThreads) void groups_kernel(uint32_t n, uint32_t tiles, uint32_t max_passes,
+                                                              Workspace w, int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ n_unique) {
+    Ctl* ctl = w.ctl;
+    if (load_status(&ctl->error) != 0u) {  // the sort gave up: report it instead of groups
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            offsets[0] = 0;
+            *n_unique = -1;
+        }
+        return;
+    }
+    __shared__ uint32_t s_tile, s_total, s_excl;
+    __shared__ uint32_t wcount[kPassWaves];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint64_t lt = (uint64_t(1) << lane) - 1u;
+    if (threadIdx.x == 0) s_tile = atomicAdd(&ctl->tile_ctr[kMaxPasses], 1u);
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    const uint32_t q = ctl->npass & 1u;  // buffer the last pass wrote
+    const bool has_hi = ctl->has_hi != 0u;
+    const uint64_t* __restrict__ lo = w.lo[q];
+    const uint64_t* __restrict__ hi = w.hi[q];
+    uint32_t* st = w.status + size_t(max_passes) * kStatusWords * tiles;  // [tiles] group counts
+
+    const uint32_t first = tile * kTile + wave * kWaveSpan;
+    uint64_t m[kItems];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kItems; ++j) {
+        const uint32_t i = first + j * 64u + lane;
+        bool f = false;
+        if (i < n) f = i == 0 || lo[i] != lo[i - 1] || (has_hi && hi[i] != hi[i - 1]);
+        m[j] = __ballot(f);
+        cnt += static_cast<uint32_t>(__popcll(m[j]));
+    }
+    if (lane == 0) wcount[wave] = cnt;
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t total = 0;
+        for (uint32_t k = 0; k < kPassWaves; ++k) total += wcount[k];
+        if (lane == 0) store_status(st + tile, kWordReady | total);
+        uint32_t acc = 0;  // groups in the earlier tiles, lane by lane
+        for (uint32_t t0 = 0; t0 < tile; t0 += 64u) {
+            const uint32_t t = t0 + lane;
+            if (t < tile) acc += wait_ready(st + t, load_status(st + t), kWordReady, &ctl->error) & ~kWordReady;
+        }
+        const uint32_t excl = wave_sum(acc);
+        if (lane == 0) {
+            s_total = total;
+            s_excl = excl;
+        }
+    }
+    __syncthreads();
+    if (load_status(&ctl->error) != 0u) {  // a wait gave up: report it instead of a count
+        if (threadIdx.x == 0) *n_unique = -1;
+        return;
+    }
+    uint32_t pos = s_excl;
+    for (uint32_t k = 0; k < wave; ++k) pos += wcount[k];
+#pragma unroll
+    for (uint32_t j = 0; j < kItems; ++j) {
+        if ((m[j] >> lane) & 1u) {
+            const uint32_t at = pos + static_cast<uint32_t>(__popcll(m[j] & lt));
+            if (at < n) offsets[at] = static_cast<int32_t>(first + j * 64u + lane);
+        }
+        pos += static_cast<uint32_t>(__popcll(m[j]));
+    }
+    if (tile == tiles - 1u && threadIdx.x == 0) {
+        const uint32_t total = s_excl + s_total;
+        if (total <= n) offsets[total] = static_cast<int32_t>(n);
+        *n_unique = static_cast<int32_t>(total);
     }
 }
 
@@ -278,50 +683,11 @@ __global__ void empty_kernel(int32_t* __restrict__ offsets, int32_t* __restrict_
     *n_unique = 0;
 }
 
-size_t align_up(size_t x) { return (x + 255u) & ~size_t(255u); }
-
-struct Workspace {
-    uint64_t* klo[2];
-    uint64_t* khi[2];
-    int32_t* val;      // second value buffer (the first is the caller's perm)
-    uint32_t* cnt;     // [256][blocks]
-    uint32_t* tot;     // [256]
-    uint32_t* bsum;    // [blocks]
-    uint32_t* total;   // [1]
-};
-
-size_t layout(uint32_t n, char* base, Workspace* w) {
-    const uint32_t blocks = (n + kTile - 1u) / kTile;
-    size_t off = 0;
-    auto take = [&](size_t bytes) {
-        char* p = base ? base + off : nullptr;
-        off += align_up(bytes);
-        return p;
-    };
-    Workspace t;
-    t.klo[0] = reinterpret_cast<uint64_t*>(take(size_t(n) * 8));
-    t.klo[1] = reinterpret_cast<uint64_t*>(take(size_t(n) * 8));
-    t.khi[0] = reinterpret_cast<uint64_t*>(take(size_t(n) * 8));
-    t.khi[1] = reinterpret_cast<uint64_t*>(take(size_t(n) * 8));
-    t.val = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
-    t.cnt = reinterpret_cast<uint32_t*>(take(size_t(256) * blocks * 4));
-    t.tot = reinterpret_cast<uint32_t*>(take(256 * 4));
-    t.bsum = reinterpret_cast<uint32_t*>(take(size_t(blocks) * 4));
-    t.total = reinterpret_cast<uint32_t*>(take(4));
-    if (w) *w = t;
-    return off;
-}
-
 }  // namespace
 
-uint32_t dedup_key_bits(uint32_t vocab_size) {
-    if (vocab_size == 0) return 31;
-    uint32_t b = 1;
-    while (b < 31 && (uint64_t(1) << b) < vocab_size) ++b;
-    return b;
+size_t dedup_workspace_bytes(uint32_t n, uint32_t vocab_size) {
+    return n == 0 ? 0 : layout(n, vocab_size, nullptr, nullptr);
 }
-
-size_t dedup_workspace_bytes(uint32_t n) { return n == 0 ? 0 : layout(n, nullptr, nullptr); }
 
 hipError_t launch_dedup(const int32_t* ids, const int32_t* history, uint32_t n, uint32_t seq_len, uint32_t vocab_size,
                         int32_t* perm, int32_t* offsets, int32_t* n_unique, void* ws, hipStream_t stream) {
@@ -330,29 +696,25 @@ hipError_t launch_dedup(const int32_t* ids, const int32_t* history, uint32_t n, 
         return hipGetLastError();
     }
     const Ids s{ids, history, seq_len};
+    const KeyPlan k = key_plan(vocab_size);
     Workspace w;
-    layout(n, static_cast<char*>(ws), &w);
-    const uint32_t bits = dedup_key_bits(vocab_size);
-    const int passes = static_cast<int>((4 * bits + 7) / 8);
-    const uint32_t blocks = (n + kTile - 1u) / kTile;
-    // Value buffers alternate so that the last pass writes the caller's perm.
-    int32_t* vbuf[2] = {perm, w.val};
-    int cur = (passes & 1) ? 1 : 0;  // buffer holding the current values
-    hipLaunchKernelGGL(build_keys_kernel, dim3((n + kThreads - 1u) / kThreads), dim3(kThreads), 0, stream, s, n, bits,
-                       w.klo[0], w.khi[0], vbuf[cur]);
-    int kc = 0;
-    for (int pass = 0; pass < passes; ++pass) {
-        hipLaunchKernelGGL(hist_kernel, dim3(blocks), dim3(kThreads), 0, stream, w.klo[kc], w.khi[kc], n, pass, w.cnt);
-        hipLaunchKernelGGL(colscan_kernel, dim3(256), dim3(1024), 0, stream, w.cnt, blocks, w.tot);
-        hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(kThreads), 0, stream, w.klo[kc], w.khi[kc], vbuf[cur], n,
-                           pass, w.cnt, w.tot, w.klo[kc ^ 1], w.khi[kc ^ 1], vbuf[cur ^ 1]);
-        kc ^= 1;
-        cur ^= 1;
-    }
-    hipLaunchKernelGGL(flag_count_kernel, dim3(blocks), dim3(kThreads), 0, stream, w.klo[kc], w.khi[kc], n, w.bsum);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, w.bsum, blocks, w.total);
-    hipLaunchKernelGGL(group_offsets_kernel, dim3(blocks), dim3(kThreads), 0, stream, w.klo[kc], w.khi[kc], n, w.bsum,
-                       w.total, offsets, n_unique);
+    layout(n, vocab_size, static_cast<char*>(ws), &w);
+    const uint32_t tiles = (n + kTile - 1u) / kTile;
+    const size_t zero_bytes =
+        reinterpret_cast<char*>(w.status + status_words(k, tiles)) - reinterpret_cast<char*>(w.hist);
+    const uint32_t zero_words = static_cast<uint32_t>(zero_bytes / sizeof(uint32_t));
+    const uint32_t init_blocks = std::min<uint32_t>(2048u, (std::max<uint32_t>(n, zero_words) + 255u) / 256u);
+    hipLaunchKernelGGL(init_kernel, dim3(init_blocks), dim3(256), 0, stream, s, n, vocab_size, uint32_t(k.compact),
+                       zero_words, w, k.bits, uint32_t(k.max_passes), uint32_t(k.hi_possible));
+    if (k.compact)
+        hipLaunchKernelGGL(bitmap_kernel, dim3((vocab_size + kRankIds - 1u) / kRankIds), dim3(256), 0, stream,
+                           vocab_size, w);
+    hipLaunchKernelGGL(keys_kernel, dim3((n + kKeyThreads * kKeyItems - 1u) / (kKeyThreads * kKeyItems)),
+                       dim3(kKeyThreads), 0, stream, s, n, vocab_size, uint32_t(k.compact), w);
+    for (int pass = 0; pass < k.max_passes; ++pass)
+        hipLaunchKernelGGL(pass_kernel, dim3(tiles), dim3(kPassThreads), 0, stream, n, pass, tiles, w, perm);
+    hipLaunchKernelGGL(groups_kernel, dim3(tiles), dim3(kPassThreads), 0, stream, n, tiles, uint32_t(k.max_passes), w,
+                       offsets, n_unique);
     return hipGetLastError();
 }
 

@@ -175,10 +175,10 @@ int engram_gather_rows(engram_plan_t p, const uint32_t* addr, int64_t n_tok, flo
     return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
 }
 
-int engram_dedup_workspace(int64_t n_tok, size_t* bytes) {
-    if (!bytes) return ENGRAM_EINVAL;
-    if (n_tok < 0 || n_tok > kMaxTokens) return ENGRAM_ERANGE;
-    *bytes = dedup_workspace_bytes(uint32_t(n_tok));
+int engram_dedup_workspace(engram_plan_t p, int64_t n_tok, size_t* bytes) {
+    if (!valid_plan(p) || !bytes) return ENGRAM_EINVAL;
+    if (n_tok < 0 || n_tok > kMaxDedupTokens) return ENGRAM_ERANGE;
+    *bytes = dedup_workspace_bytes(uint32_t(n_tok), p->vocab_size);
     return ENGRAM_OK;
 }
 
@@ -189,12 +189,13 @@ int engram_dedup(engram_plan_t p, const int32_t* ids, const int32_t* history, in
     int64_t n_tok = 0;
     int st = check_tokens(n_seq, seq_len, &n_tok);
     if (st != ENGRAM_OK) return st;
+    if (n_tok > kMaxDedupTokens) return ENGRAM_ERANGE;
     if (!offsets || !n_unique || !aligned(offsets, 4) || !aligned(n_unique, 4)) return ENGRAM_EINVAL;
     if (n_tok > 0) {
         if (!ids || !perm || !aligned(ids, 4) || !aligned(perm, 4)) return ENGRAM_EINVAL;
         if (history && !aligned(history, 4)) return ENGRAM_EINVAL;
     }
-    const size_t need = dedup_workspace_bytes(uint32_t(n_tok));
+    const size_t need = dedup_workspace_bytes(uint32_t(n_tok), p->vocab_size);
     if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return ENGRAM_EWORKSPACE;
     hipError_t e = launch_dedup(ids, history, uint32_t(n_tok), uint32_t(seq_len), p->vocab_size, perm, offsets,
                                 n_unique, ws, static_cast<hipStream_t>(stream));

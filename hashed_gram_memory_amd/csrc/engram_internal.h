@@ -74,9 +74,12 @@ hipError_t launch_lookup(const HashParams& h, const GatherParams& g, const int32
 hipError_t launch_gate_io(const GatherParams& p, const uint32_t* addr, const float* weights, uint32_t n_tok,
                           float* out, hipStream_t stream);
 
-size_t dedup_workspace_bytes(uint32_t n_tok);
+// Workspace bytes of launch_dedup for n_tok tokens under a vocabulary bound (0 = none).
+size_t dedup_workspace_bytes(uint32_t n_tok, uint32_t vocab_size);
 
-uint32_t dedup_key_bits(uint32_t vocab_size);
+// Tokens per dedup call.  Each tile of the sort reads the published counts of
+// all earlier tiles, a cost that grows with the square of the tile count.
+constexpr int64_t kMaxDedupTokens = (int64_t(1) << 22);
 
 hipError_t launch_dedup(const int32_t* ids, const int32_t* history, uint32_t n_tok, uint32_t seq_len,
                         uint32_t vocab_size, int32_t* perm, int32_t* offsets, int32_t* n_unique, void* ws,

@@ -40,7 +40,7 @@ namespace {
 
 template <bool kDedup, int FMT>
 __global__ __launch_bounds__(256) void gather_reduce_kernel(const GatherParams P, const uint32_t* __restrict__ addr,
-                                                            uint32_t item_base, uint32_t n_items,
+                                                            uint32_t item_base, uint32_t item_end, uint32_t n_tok,
                                                             const int32_t* __restrict__ perm,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ n_unique,
@@ -52,12 +52,20 @@ __global__ __launch_bounds__(256) void gather_reduce_kernel(const GatherParams P
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t item = item_base + group * 4u + wave;
 
-    uint32_t limit = n_items;
-    if (kDedup) limit = min(limit, static_cast<uint32_t>(*n_unique));
+    uint32_t limit = item_end;
+    if (kDedup) {
+        const int32_t nu = *n_unique;  // negative: the dedup call failed, there are no groups
+        limit = nu > 0 ? min(limit, static_cast<uint32_t>(nu)) : 0u;
+    }
     if (item >= limit) return;
 
     uint32_t tok = item;
-    if (kDedup) tok = static_cast<uint32_t>(perm[offsets[item]]);
+    if (kDedup) {
+        const uint32_t first = static_cast<uint32_t>(offsets[item]);
+        if (first >= n_tok) return;
+        tok = static_cast<uint32_t>(perm[first]);
+        if (tok >= n_tok) return;
+    }
     const uint32_t s0 = module * kRowsPerModule;
     // lane q < 24 takes the address of the module's row q (one coalesced load)
     const uint32_t a = addr[static_cast<size_t>(tok) * kSub + s0 + owned_row(lane)];
@@ -73,20 +81,21 @@ __global__ __launch_bounds__(256) void gather_reduce_kernel(const GatherParams P
         // first store is unconditional; a loop that could run zero times
         // would let the compiler sink the loads below a branch that the
         // row-base broadcasts cannot follow, keeping all 24 live at once.
-        int32_t i = offsets[item];
-        const int32_t end = offsets[item + 1];
+        uint32_t i = static_cast<uint32_t>(offsets[item]);
+        const uint32_t end = min(static_cast<uint32_t>(offsets[item + 1]), n_tok);
         do {
             const uint32_t t = static_cast<uint32_t>(perm[i]);
-            __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(t) * (2 * kRowBytes) + col));
+            if (t < n_tok)
+                __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(t) * (2 * kRowBytes) + col));
         } while (++i < end);
     }
 }
 
 template <bool kDedup, int FMT>
 void launch_one(const GatherParams& p, dim3 grid, hipStream_t stream, const uint32_t* addr, uint32_t base, uint32_t end,
-                const int32_t* perm, const int32_t* offsets, const int32_t* n_unique, float* out) {
-    hipLaunchKernelGGL((gather_reduce_kernel<kDedup, FMT>), grid, dim3(256), 0, stream, p, addr, base, end, perm, offsets,
-                       n_unique, out);
+                uint32_t n_tok, const int32_t* perm, const int32_t* offsets, const int32_t* n_unique, float* out) {
+    hipLaunchKernelGGL((gather_reduce_kernel<kDedup, FMT>), grid, dim3(256), 0, stream, p, addr, base, end, n_tok, perm,
+                       offsets, n_unique, out);
 }
 
 }  // namespace
@@ -104,13 +113,13 @@ hipError_t launch_gather_reduce(const GatherParams& p, const uint32_t* addr, uin
         const uint32_t groups = ((n + 3u) / 4u + 3u) & ~3u;
         const dim3 grid(2u * groups);
         if (perm && mx)
-            launch_one<true, ENGRAM_SCALE_E8M0_BLOCK32>(p, grid, stream, addr, base, base + n, perm, offsets, n_unique, out);
+            launch_one<true, ENGRAM_SCALE_E8M0_BLOCK32>(p, grid, stream, addr, base, base + n, n_tok, perm, offsets, n_unique, out);
         else if (perm)
-            launch_one<true, ENGRAM_SCALE_F32_ROW>(p, grid, stream, addr, base, base + n, perm, offsets, n_unique, out);
+            launch_one<true, ENGRAM_SCALE_F32_ROW>(p, grid, stream, addr, base, base + n, n_tok, perm, offsets, n_unique, out);
         else if (mx)
-            launch_one<false, ENGRAM_SCALE_E8M0_BLOCK32>(p, grid, stream, addr, base, base + n, perm, offsets, n_unique, out);
+            launch_one<false, ENGRAM_SCALE_E8M0_BLOCK32>(p, grid, stream, addr, base, base + n, n_tok, perm, offsets, n_unique, out);
         else
-            launch_one<false, ENGRAM_SCALE_F32_ROW>(p, grid, stream, addr, base, base + n, perm, offsets, n_unique, out);
+            launch_one<false, ENGRAM_SCALE_F32_ROW>(p, grid, stream, addr, base, base + n, n_tok, perm, offsets, n_unique, out);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

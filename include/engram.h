@@ -11,6 +11,9 @@
  *   [REQ]   "Running DeepSeek V4.1 Flash locally: the numbers beyond 552B",
  *           section "Backbone, Engram, and active parameters describe
  *           different scales"
+ *   [X]     "How DeepSeek V4.1 Flash's 763B weights run on consumer GPUs"
+ *   [BLOG]  stondo.github.io, "deepseek-v41-flash-552b-exl3-two-rtx-pro-6000",
+ *           section "What eager-plus-NVMe actually delivers"
  *
  * The operation.  Two Engram modules each hash the suffix n-grams of order
  * 2, 3 and 4 of the token-id stream with 8 independent heads and read one
@@ -82,9 +85,13 @@ typedef enum engram_status {
  *       Must equal 2, 2, 4, 8, 256 (else ENGRAM_EUNSUPPORTED).
  *   vocab_size
  *       Exclusive upper bound of the token ids (the vocabulary the ids are
- *       drawn from), or 0 when ids may take any value in [0, 2^31).  Only
- *       engram_dedup uses it: it packs a window into 4*ceil(log2(vocab_size))
- *       bits, so an id >= vocab_size breaks its grouping (not checked).
+ *       drawn from), or 0 when ids may take any value in [0, 2^31).  It is
+ *       the length of vocab_map when there is one.  engram_dedup uses it to
+ *       size its sort keys: 4*ceil(log2(vocab_size)) bits per window, or, for
+ *       2^16 < vocab_size <= 2^18, 4*ceil(log2(D+1)) bits where D is the
+ *       number of distinct ids the call uses.  Ids at or above vocab_size
+ *       break the dedup grouping and, with a vocab_map, the hash (see
+ *       engram_hash); engram_check_inputs counts them.
  *   hash_seed
  *       Seeds the 192 hash multipliers: M[i] is output i+1 of splitmix64
  *       (Steele, Lea and Flood 2014) seeded with hash_seed, with bit 0 set;
@@ -145,9 +152,15 @@ int engram_plan_desc_init(engram_plan_desc* desc);
 /*
  * Validate a description and build an immutable plan: copies the row counts
  * and pointers, derives the multipliers and the exact division constants of
- * each R_s.  Host-only: touches no device and may run before any device
- * exists.  *out is set only on ENGRAM_OK.  A plan may be used from several
- * host threads and streams at once.
+ * each R_s.  The geometry it accepts is the pages' one: two modules, orders
+ * 2 to 4, 8 heads per order, 256-byte FP8 rows, 48 sub-tables [GUIDE
+ * "Engram"; VRAM].  The pages print no hash constants; the multipliers are
+ * this library's own (see hash_seed).  Host-only: touches no device and may
+ * run before any device exists.  *out is set only on ENGRAM_OK.  A plan may
+ * be used from several host threads and streams at once.  Errors: EINVAL
+ * (NULL argument, pointer, misaligned pointer, reserved1 != 0, a vocab_map
+ * without vocab_size), ERANGE (a row count of 0 or above 2^32),
+ * EUNSUPPORTED (another geometry or scale format).
  */
 int engram_plan(const engram_plan_desc* desc, engram_plan_t* out);
 
@@ -169,9 +182,12 @@ int engram_plan_multipliers(engram_plan_t plan, uint64_t* out);
  *     x = XOR_{k<n} ( u64(w_k) * M[m][n][h][k] )   (mod 2^64)
  *     addr[tok][24*m + 8*(n-2) + h] = x mod R_s
  *
- *   ids      device int32 [n_seq][seq_len], ids in [0, 2^31); not checked on
- *            the device (a negative id is a contract violation).
- *   history  device int32 [n_seq][3] or NULL.
+ *   ids      device int32 [n_seq][seq_len], ids in [0, 2^31), and below the
+ *            plan's vocab_size when it has a vocab_map (the map is read at
+ *            every window id, history and pad included, without a bounds
+ *            check: a larger or negative id reads outside the map).  Not
+ *            checked on the device; engram_check_inputs counts violations.
+ *   history  device int32 [n_seq][3] or NULL; the same bounds as ids.
  *   addr     device uint32 [n_seq*seq_len][48], 16-byte aligned (output).
  *
  * n_seq*seq_len == 0 is a no-op.  Errors: EINVAL (NULL/misaligned pointer,
@@ -270,29 +286,47 @@ int engram_lookup(engram_plan_t plan, const int32_t* ids, const int32_t* history
                   int64_t n_seq, int64_t seq_len, float* out, void* stream);
 
 /*
- * Workspace bytes engram_dedup needs for n_tok tokens (host-only).
+ * Workspace bytes engram_dedup needs for n_tok tokens under this plan
+ * (host-only).  The size depends on the plan's vocab_size, which bounds the
+ * width of the sort keys.  Errors: EINVAL (NULL plan or bytes), ERANGE
+ * (n_tok < 0 or > 2^22).
  */
-int engram_dedup_workspace(int64_t n_tok, size_t* bytes);
+int engram_dedup_workspace(engram_plan_t plan, int64_t n_tok, size_t* bytes);
 
 /*
- * Group the tokens whose id windows (w_0, w_1, w_2, w_3) are equal: they
- * hash to the same 48 rows, so one lookup serves the whole group.  This
- * serves batches of prompts that share a prefix.  Groups are ordered by
- * ascending window (w_0 most significant, ids compared as unsigned), tokens
- * within a group by ascending index: the result is unique.
+ * Group the tokens whose id windows (w_0, w_1, w_2, w_3) are equal.
  *
- *   ids, history, n_seq, seq_len   as for engram_hash.
+ * The pages hash every row address from the token ids alone, before the
+ * forward pass, so a whole batch's addresses are known up front and can be
+ * fetched together [VRAM]; and in the serving setups they describe, most of
+ * a prompt is a prefix other requests already sent [BLOG "What eager-plus-
+ * NVMe actually delivers"].  Tokens with equal windows hash to the same 48
+ * rows, so one lookup serves a whole group (engram_gather_reduce in dedup
+ * mode).  Groups are ordered by ascending window (w_0 most significant, ids
+ * compared as unsigned), tokens within a group by ascending index: the
+ * result is unique.
+ *
+ *   ids, history, n_seq, seq_len   as for engram_hash.  Every id should be
+ *             < the plan's vocab_size (when it is not 0); a larger or negative
+ *             id is a contract violation: its grouping is then unspecified,
+ *             but the call reads and writes nothing out of bounds.
  *   perm      device int32 [n_tok]: the tokens, group by group (output).
  *   offsets   device int32 [n_tok + 1]: offsets[u] is where group u starts
  *             in perm; offsets[n_unique] = n_tok; entries past n_unique are
  *             left unspecified (output).
- *   n_unique  device int32 [1]: the number of groups (output).
- *   ws        device workspace of ws_bytes >= engram_dedup_workspace(n_tok),
- *             256-byte aligned, owned by the caller, reusable after the
- *             stream passes this call.
+ *   n_unique  device int32 [1]: the number of groups (output).  -1 reports
+ *             that a bounded device-side wait of the sort gave up (the sort's
+ *             tiles wait for the ones started before them; this does not
+ *             happen unless the device stalls a running workgroup for
+ *             milliseconds): perm and offsets are then invalid, and
+ *             engram_gather_reduce in dedup mode treats the groups as empty.
+ *   ws        device workspace of ws_bytes >= engram_dedup_workspace(plan,
+ *             n_tok), 256-byte aligned, owned by the caller.  It keeps a
+ *             small state between calls (no clearing needed, initial
+ *             contents arbitrary); one call at a time may use it.
  *
  * n_tok == 0 writes offsets[0] = 0 and *n_unique = 0.  Errors: EINVAL,
- * ERANGE, EWORKSPACE.
+ * ERANGE (n_tok > 2^22 = 4,194,304: split larger batches), EWORKSPACE.
  */
 int engram_dedup(engram_plan_t plan, const int32_t* ids, const int32_t* history,
                  int64_t n_seq, int64_t seq_len, int32_t* perm, int32_t* offsets,

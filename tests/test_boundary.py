@@ -159,10 +159,15 @@ def test_gather_reduce_validation(hg, plan):
 def test_dedup_validation(hg, plan):
     L = hg.lib()
     b = ctypes.c_size_t()
-    assert L.engram_dedup_workspace(-1, ctypes.byref(b)) == ERANGE
-    assert L.engram_dedup_workspace(1, None) == EINVAL
-    assert L.engram_dedup_workspace(1000, ctypes.byref(b)) == OK
+    assert L.engram_dedup_workspace(plan, -1, ctypes.byref(b)) == ERANGE
+    assert L.engram_dedup_workspace(plan, (1 << 22) + 1, ctypes.byref(b)) == ERANGE
+    assert L.engram_dedup_workspace(plan, 1 << 22, ctypes.byref(b)) == OK
+    assert L.engram_dedup_workspace(plan, 1, None) == EINVAL
+    assert L.engram_dedup_workspace(None, 1, ctypes.byref(b)) == EINVAL
+    assert L.engram_dedup_workspace(plan, 0, ctypes.byref(b)) == OK and b.value == 0
+    assert L.engram_dedup_workspace(plan, 1000, ctypes.byref(b)) == OK
     need = b.value
+    assert need > 0
     if need:
         assert L.engram_dedup(plan, FAKE, None, 1, 1000, FAKE, FAKE, FAKE, None, need, None) == EWORKSPACE
         assert L.engram_dedup(plan, FAKE, None, 1, 1000, FAKE, FAKE, FAKE, FAKE, need - 1, None) == EWORKSPACE
@@ -172,6 +177,7 @@ def test_dedup_validation(hg, plan):
     assert L.engram_dedup(plan, FAKE, None, 1, 1000, FAKE, FAKE, None, FAKE, need, None) == EINVAL
     assert L.engram_dedup(plan, FAKE, None, -1, 1000, FAKE, FAKE, FAKE, FAKE, need, None) == EINVAL
     assert L.engram_dedup(None, FAKE, None, 1, 1000, FAKE, FAKE, FAKE, FAKE, need, None) == EINVAL
+    assert L.engram_dedup(plan, FAKE, None, 1 << 11, (1 << 11) + 1, FAKE, FAKE, FAKE, FAKE, need, None) == ERANGE
 
 
 def test_synth_fill_validation(hg):

@@ -106,7 +106,7 @@ def test_dedup_pipeline_graph_replay_matches_eager():
     groups = lib().Groups(torch.empty(n_tok, dtype=torch.int32, device="cuda"),
                           torch.empty(n_tok + 1, dtype=torch.int32, device="cuda"),
                           torch.empty(1, dtype=torch.int32, device="cuda"))
-    ws = torch.empty(lib().dedup_workspace_bytes(n_tok), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(lib().dedup_workspace_bytes(plan, n_tok), dtype=torch.uint8, device="cuda")
 
     def step():
         lib().hash(plan, d_ids, out=addr)
@@ -152,3 +152,63 @@ def test_dedup_batched_shared_prefix_full_size():
     _say(f"n_unique={nu} of {w.n_tok}")
     assert nu < w.n_tok * 0.6
     assert torch.equal(dd, direct)
+
+
+def test_dedup_wide_keys_many_ids():
+    """300,000 tokens uniform over a 129,280-id vocabulary use more than 2^16 distinct ids, so the compacted keys
+    need 17 bits per id: 68-bit keys and a ninth pass over the high key word."""
+    _say("dedup 3 x 100000 uniform ids, vocab 129280 (keys above 64 bits)")
+    rng = np.random.default_rng(68)
+    ids = rng.integers(0, 129280, size=(3, 100000), dtype=np.int64).astype(np.int32)
+    plan = dummy_plan(4096, 129280)
+    groups = lib().dedup(plan, *to_dev_ids(ids, None))
+    torch.cuda.synchronize()
+    _check_groups(groups, ids, None)
+
+
+def _ws_ids_in_use(ws):
+    """The number of distinct ids the last compacting dedup call counted (a word of the workspace's control
+    block, at byte 16)."""
+    return int(ws[16:20].cpu().numpy().view(np.uint32)[0])
+
+
+def test_dedup_workspace_state_across_calls():
+    """The workspace is not cleared between calls: ids of an earlier call are not counted again, an arbitrary
+    initial content is harmless, and a content that marks every id as in use still gives exact groups."""
+    _say("dedup workspace reuse")
+    plan = dummy_plan(4096, 129280)
+    rng = np.random.default_rng(70)
+    n_seq, seq_len = 4, 5000
+    ws = torch.empty(lib().dedup_workspace_bytes(plan, n_seq * seq_len), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)
+    for rep, hi in enumerate((129280, 500, 129280, 37)):
+        ids = rng.integers(0, hi, size=(n_seq, seq_len), dtype=np.int64).astype(np.int32)
+        groups = lib().dedup(plan, *to_dev_ids(ids, None), workspace=ws)
+        torch.cuda.synchronize()
+        _check_groups(groups, ids, None)
+        used = np.unique(np.concatenate([ids.ravel(), [0]])).size  # the ids plus the pad id 0
+        if rep > 0:  # the first call may count stale entries of the 0xA5 fill
+            assert _ws_ids_in_use(ws) == used, rep
+    # every presence entry equal to the next call's stamp: all 129,280 ids count as in use (17-bit ids)
+    words = ws.view(torch.int32)
+    words.fill_(7)
+    words[0] = 6  # the stamp of the "previous" call
+    ids = rng.integers(0, 1000, size=(n_seq, seq_len), dtype=np.int64).astype(np.int32)
+    groups = lib().dedup(plan, *to_dev_ids(ids, None), workspace=ws)
+    torch.cuda.synchronize()
+    assert _ws_ids_in_use(ws) == 129280
+    _check_groups(groups, ids, None)
+
+
+@pytest.mark.parametrize("vocab", [65536, 65537, 1 << 18, (1 << 18) + 1])
+def test_dedup_vocab_bounds_of_compaction(vocab):
+    """Vocabulary sizes at both edges of the compacted-key range give exact groups."""
+    _say(f"dedup vocab {vocab}")
+    rng = np.random.default_rng(vocab % 1000)
+    ids = rng.integers(0, vocab, size=(5, 3001), dtype=np.int64).astype(np.int32)
+    ids[:, :50] = vocab - 1 - np.arange(50)
+    hist = rng.integers(0, vocab, size=(5, 3), dtype=np.int64).astype(np.int32)
+    plan = dummy_plan(4096, vocab)
+    groups = lib().dedup(plan, *to_dev_ids(ids, hist))
+    torch.cuda.synchronize()
+    _check_groups(groups, ids, hist)
