@@ -79,6 +79,7 @@ def _load():
         "engram_gather_rows": [P, VP, I64, VP, VP],
         "engram_dedup_workspace": [P, I64, ctypes.POINTER(ctypes.c_size_t)],
         "engram_dedup": [P, VP, VP, I64, I64, VP, VP, VP, VP, ctypes.c_size_t, VP],
+        "engram_dedup_noalloc": [P, VP, VP, I64, I64, VP, VP, VP, VP],
         "engram_synth_fill": [VP, VP, U64, U32, U64, VP],
         "engram_synth_fill_e8m0": [VP, U64, U32, U64, VP],
         "engram_probe_read": [VP, U64, VP, VP],
@@ -392,6 +393,29 @@ def dedup(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, wo
                            _dev(groups.n_unique, torch.int32, "n_unique"), _dev(workspace, torch.uint8, "workspace"),
                            workspace.numel(), _stream(stream))
     _check(st, "engram_dedup")
+    return groups
+
+
+DEDUP_SCRATCH_BYTES = 32 << 20
+
+
+def dedup_noalloc(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, groups: Groups | None = None,
+                  stream=None) -> Groups:
+    """dedup with the library's fixed device workspace (engram_dedup_noalloc): the call allocates nothing when
+    ``groups`` is given.  Calls that overlap on one GPU race."""
+    n_seq, seq_len = _ids_shape(ids, history)
+    n_tok = n_seq * seq_len
+    if groups is None:
+        groups = Groups(torch.empty(n_tok, dtype=torch.int32, device=ids.device),
+                        torch.empty(n_tok + 1, dtype=torch.int32, device=ids.device),
+                        torch.empty(1, dtype=torch.int32, device=ids.device))
+    else:
+        _check_groups(groups, n_tok)
+    st = _lib.engram_dedup_noalloc(plan.handle, _dev(ids, torch.int32, "ids"),
+                                   None if history is None else _dev(history, torch.int32, "history"), n_seq, seq_len,
+                                   _dev(groups.perm, torch.int32, "perm"), _dev(groups.offsets, torch.int32, "offsets"),
+                                   _dev(groups.n_unique, torch.int32, "n_unique"), _stream(stream))
+    _check(st, "engram_dedup_noalloc")
     return groups
 
 

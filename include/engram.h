@@ -332,6 +332,25 @@ int engram_dedup(engram_plan_t plan, const int32_t* ids, const int32_t* history,
                  int64_t n_seq, int64_t seq_len, int32_t* perm, int32_t* offsets,
                  int32_t* n_unique, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * engram_dedup for callers that cannot allocate device memory (code under
+ * HIP graph capture that forbids allocation, tight serving loops, harnesses
+ * that disallow hipMalloc): the same kernels and results, with the workspace
+ * in a fixed array of ENGRAM_DEDUP_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends.  The call itself allocates
+ * nothing.  Arguments, outputs and errors are those of engram_dedup, without
+ * ws and ws_bytes; a batch whose workspace (engram_dedup_workspace) exceeds
+ * the fixed size returns ENGRAM_EWORKSPACE before anything is launched
+ * (524,288 tokens fit under any plan).  All calls on one GPU share that
+ * GPU's array: calls that overlap in time on one GPU (two streams, two host
+ * threads) race and give wrong groups; serialise them.  The first call on a
+ * device looks up the array's address there (hipGetSymbolAddress).
+ */
+#define ENGRAM_DEDUP_SCRATCH_BYTES (32u << 20)
+int engram_dedup_noalloc(engram_plan_t plan, const int32_t* ids, const int32_t* history,
+                         int64_t n_seq, int64_t seq_len, int32_t* perm, int32_t* offsets,
+                         int32_t* n_unique, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* engram_status_string(int status);
 

@@ -336,3 +336,21 @@ def test_binding_rejects_groups_of_another_size(hg):
             hg.dedup(None, ids, groups=g)
         with pytest.raises(ValueError, match="groups"):
             hg.gather_reduce(None, addr, groups=g)
+
+
+def test_dedup_noalloc_validation(hg, plan):
+    """engram_dedup_noalloc validates on the host like engram_dedup and refuses, before any launch, a batch whose
+    workspace exceeds its fixed device array."""
+    L = hg.lib()
+    assert L.engram_dedup_noalloc(None, FAKE, None, 1, 10, FAKE, FAKE, FAKE, None) == EINVAL
+    assert L.engram_dedup_noalloc(plan, FAKE, None, -1, 10, FAKE, FAKE, FAKE, None) == EINVAL
+    assert L.engram_dedup_noalloc(plan, FAKE, None, 1, 10, None, FAKE, FAKE, None) == EINVAL
+    assert L.engram_dedup_noalloc(plan, FAKE, None, 1, 10, FAKE, FAKE + 2, FAKE, None) == EINVAL
+    assert L.engram_dedup_noalloc(plan, FAKE, None, 1 << 11, (1 << 11) + 1, FAKE, FAKE, FAKE, None) == ERANGE
+    # a batch whose workspace is above the fixed size: the plan fixture has vocab_size 0 (31-bit ids, the widest keys)
+    b = ctypes.c_size_t()
+    n = 1 << 22
+    assert L.engram_dedup_workspace(plan, n, ctypes.byref(b)) == OK and b.value > hg.DEDUP_SCRATCH_BYTES
+    assert L.engram_dedup_noalloc(plan, FAKE, None, 1, n, FAKE, FAKE, FAKE, None) == EWORKSPACE
+    # the size the fixed array is stated to hold under any plan
+    assert L.engram_dedup_workspace(plan, 524288, ctypes.byref(b)) == OK and b.value <= hg.DEDUP_SCRATCH_BYTES
