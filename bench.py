@@ -7,8 +7,12 @@ vocabulary, 48 sub-tables x 2^24 rows x 256 B FP8 E4M3 (192 GiB) plus fp32
 row scales, resident in HBM and filled on the device from a seeded
 generator.  Inputs are resident before the timed region starts.
 
-Prints one JSON line.  Extra figures (roofline of the gather kernel, the CPU
-oracle timed on a bounded sample of the same workload) ride in that line.
+Prints one JSON line.  Extra figures ride in that line: the roofline of the
+gather kernel (algorithmic bytes over its HIP-event time, and the bytes the
+request-size counters saw leave L2), two control timings of the gather
+(uniform ids, caches flushed), the same step as one fused launch and under
+HIP-graph replay, memory-ceiling probes, and the CPU oracle timed on whole
+workloads with one process and with the host's cores.
 """
 from __future__ import annotations
 
@@ -379,7 +383,10 @@ def main(argv=None) -> int:
     def hash_phase(i):
         b = batches[i % len(batches)]
         hg.hash(plan, b[1], b[2], out=addr, stream=stream)
+
+    def dedup_phase(i):
         if args.dedup:
+            b = batches[i % len(batches)]
             hg.dedup(plan, b[1], b[2], workspace=ws, groups=groups, stream=stream)
 
     # a batch of sequences is gathered in the batch order (engram_gather_reduce_batched): same results, and
@@ -397,6 +404,7 @@ def main(argv=None) -> int:
 
     def step(i):
         hash_phase(i)
+        dedup_phase(i)
         gather_phase()
 
     _log(f"warmup {args.warmup}")
@@ -404,7 +412,7 @@ def main(argv=None) -> int:
         step(i)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     flush = torch.ones(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib > 0 else None
     flush_sink = torch.zeros((), dtype=torch.uint8, device=dev)
     _log(f"timing {args.steps} steps")
@@ -417,8 +425,10 @@ def main(argv=None) -> int:
         e[0].record(stream)
         hash_phase(i)
         e[1].record(stream)
-        gather_phase()
+        dedup_phase(i)
         e[2].record(stream)
+        gather_phase()
+        e[3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -513,7 +523,8 @@ def main(argv=None) -> int:
     distinct = int(np.unique(keys).size)
 
     hash_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    gather_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    dedup_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if args.dedup else None
+    gather_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
     ms_per_step = wall / args.steps * 1e3
     tok_s = n_tok / (ms_per_step / 1e3)
     n_unique = int(groups.n_unique.item()) if args.dedup else None
@@ -587,6 +598,7 @@ def main(argv=None) -> int:
                         "graph_fused": None if graph is None else graph["fused_us_per_step"]},
         "gather_ms": gather_ms,
         "hash_ms": hash_ms,
+        "dedup_ms": dedup_ms,
         "us_per_step": ms_per_step * 1e3,
         "hash_gbps": HASH_BYTES_PER_TOKEN * n_tok / (hash_ms / 1e3) / 1e9,
         "gather_bytes_per_launch": gather_bytes,

@@ -80,6 +80,7 @@ def _load():
         "engram_dedup_workspace": [P, I64, ctypes.POINTER(ctypes.c_size_t)],
         "engram_dedup": [P, VP, VP, I64, I64, VP, VP, VP, VP, ctypes.c_size_t, VP],
         "engram_dedup_noalloc": [P, VP, VP, I64, I64, VP, VP, VP, VP],
+        "engram_check_inputs": [P, VP, VP, I64, I64, VP, I64, VP, VP],
         "engram_synth_fill": [VP, VP, U64, U32, U64, VP],
         "engram_synth_fill_e8m0": [VP, U64, U32, U64, VP],
         "engram_probe_read": [VP, U64, VP, VP],
@@ -394,6 +395,35 @@ def dedup(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, wo
                            workspace.numel(), _stream(stream))
     _check(st, "engram_dedup")
     return groups
+
+
+def check_inputs(plan: Plan, ids: torch.Tensor | None = None, history: torch.Tensor | None = None,
+                 addr: torch.Tensor | None = None, counts: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Count contract violations without faulting (engram_check_inputs): device int32 [3] = (negative ids, ids at or
+    above the plan's vocab_size, addresses at or above their sub-table's row count)."""
+    n_seq = seq_len = 0
+    if ids is not None:
+        n_seq, seq_len = _ids_shape(ids, history)
+    elif history is not None:
+        raise ValueError("history needs ids")
+    n_addr = 0
+    if addr is not None:
+        if addr.dim() != 2 or addr.shape[1] != N_SUB:
+            raise ValueError("addr must be [n_tok, 48]")
+        n_addr = addr.shape[0]
+    dev = (ids if ids is not None else addr).device if (ids is not None or addr is not None) else None
+    if counts is None:
+        if dev is None:
+            raise ValueError("nothing to check")
+        counts = torch.empty(3, dtype=torch.int32, device=dev)
+    elif counts.numel() < 3:
+        raise ValueError("counts must hold 3 int32")
+    st = _lib.engram_check_inputs(plan.handle, None if ids is None else _dev(ids, torch.int32, "ids"),
+                                  None if history is None else _dev(history, torch.int32, "history"), n_seq, seq_len,
+                                  None if addr is None else _dev(addr, torch.uint32, "addr"), n_addr,
+                                  _dev(counts, torch.int32, "counts"), _stream(stream))
+    _check(st, "engram_check_inputs")
+    return counts
 
 
 DEDUP_SCRATCH_BYTES = 32 << 20

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libengram.so")
 DEMO_SRC = os.path.join(CSRC, "examples", "c_abi_demo.c")
 DEMO = os.path.join(HERE, "c_abi_demo")
 SOURCES = ["engram_api.cpp", "hash.hip", "gather_reduce.hip", "dedup.hip", "synth_fill.hip", "probe.hip", "lookup.hip", "gate_io.hip", "gather_batched.hip",
-           "dedup_noalloc.hip"]
+           "dedup_noalloc.hip", "check.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.

@@ -202,6 +202,22 @@ int engram_dedup(engram_plan_t p, const int32_t* ids, const int32_t* history, in
     return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
 }
 
+int engram_check_inputs(engram_plan_t p, const int32_t* ids, const int32_t* history, int64_t n_seq, int64_t seq_len,
+                        const uint32_t* addr, int64_t n_addr_tok, int32_t* counts, void* stream) {
+    if (!valid_plan(p)) return ENGRAM_EINVAL;
+    int64_t n_tok = 0;
+    int st = check_tokens(n_seq, seq_len, &n_tok);
+    if (st != ENGRAM_OK) return st;
+    if (n_addr_tok < 0 || n_addr_tok > kMaxTokens) return ENGRAM_ERANGE;
+    if (!counts || !aligned(counts, 4)) return ENGRAM_EINVAL;
+    if (ids && !aligned(ids, 4)) return ENGRAM_EINVAL;
+    if (history && (!ids || !aligned(history, 4))) return ENGRAM_EINVAL;
+    if (addr && !aligned(addr, 16)) return ENGRAM_EINVAL;
+    hipError_t e = launch_check(p->hash, p->vocab_size, ids, uint64_t(n_tok), history, uint64_t(n_seq) * 3u, addr,
+                                addr ? uint64_t(n_addr_tok) : 0u, counts, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
+}
+
 const char* engram_status_string(int status) {
     switch (status) {
         case ENGRAM_OK: return "ENGRAM_OK";

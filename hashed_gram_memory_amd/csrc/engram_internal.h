@@ -85,4 +85,9 @@ hipError_t launch_dedup(const int32_t* ids, const int32_t* history, uint32_t n_t
                         uint32_t vocab_size, int32_t* perm, int32_t* offsets, int32_t* n_unique, void* ws,
                         hipStream_t stream);
 
+// Counts into counts[3] (cleared first): negative ids, ids >= vocab (vocab > 0), addresses >= R_s.
+hipError_t launch_check(const HashParams& h, uint32_t vocab, const int32_t* ids, uint64_t n_ids,
+                        const int32_t* history, uint64_t n_hist, const uint32_t* addr, uint64_t n_addr_tok,
+                        int32_t* counts, hipStream_t stream);
+
 }  // namespace engram

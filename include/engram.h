@@ -333,6 +333,31 @@ int engram_dedup(engram_plan_t plan, const int32_t* ids, const int32_t* history,
                  int32_t* n_unique, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Opt-in input check: count, on the device and without faulting, the
+ * contract violations the lookup calls do not check: the row addresses are
+ * read as given [GUIDE "Engram"], and ids index the vocabulary map.  Reads
+ * only ids, history and addr (never a table or the map), so it is safe on
+ * any values.
+ *
+ *   ids, history, n_seq, seq_len   as for engram_hash, or ids == NULL (then
+ *             history must be NULL too) to skip the id check.
+ *   addr      device uint32 [n_addr_tok][48] as engram_hash writes it,
+ *             16-byte aligned, or NULL to skip the address check.
+ *   counts    device int32 [3], 4-byte aligned (output, overwritten):
+ *             counts[0] = ids and history ids below 0,
+ *             counts[1] = ids and history ids >= the plan's vocab_size
+ *                         (always 0 when vocab_size is 0),
+ *             counts[2] = addresses addr[t][s] >= R_s.
+ *
+ * Two launches on the stream (clear, count); no synchronisation.  Errors:
+ * EINVAL (NULL plan or counts, misaligned pointer, history without ids),
+ * ERANGE (a token count out of range).
+ */
+int engram_check_inputs(engram_plan_t plan, const int32_t* ids, const int32_t* history,
+                        int64_t n_seq, int64_t seq_len, const uint32_t* addr, int64_t n_addr_tok,
+                        int32_t* counts, void* stream);
+
+/*
  * engram_dedup for callers that cannot allocate device memory (code under
  * HIP graph capture that forbids allocation, tight serving loops, harnesses
  * that disallow hipMalloc): the same kernels and results, with the workspace

@@ -354,3 +354,16 @@ def test_dedup_noalloc_validation(hg, plan):
     assert L.engram_dedup_noalloc(plan, FAKE, None, 1, n, FAKE, FAKE, FAKE, None) == EWORKSPACE
     # the size the fixed array is stated to hold under any plan
     assert L.engram_dedup_workspace(plan, 524288, ctypes.byref(b)) == OK and b.value <= hg.DEDUP_SCRATCH_BYTES
+
+
+def test_check_inputs_validation(hg, plan):
+    L = hg.lib()
+    assert L.engram_check_inputs(None, FAKE, None, 1, 1, FAKE, 1, FAKE, None) == EINVAL
+    assert L.engram_check_inputs(plan, FAKE, None, 1, 1, FAKE, 1, None, None) == EINVAL
+    assert L.engram_check_inputs(plan, FAKE, None, 1, 1, FAKE, 1, FAKE + 2, None) == EINVAL
+    assert L.engram_check_inputs(plan, FAKE + 2, None, 1, 1, None, 0, FAKE, None) == EINVAL
+    assert L.engram_check_inputs(plan, None, FAKE, 1, 1, None, 0, FAKE, None) == EINVAL  # history needs ids
+    assert L.engram_check_inputs(plan, None, None, 0, 0, FAKE + 4, 1, FAKE, None) == EINVAL  # addr 16-byte aligned
+    assert L.engram_check_inputs(plan, FAKE, None, -1, 1, None, 0, FAKE, None) == EINVAL
+    assert L.engram_check_inputs(plan, FAKE, None, 1 << 16, 1 << 15, None, 0, FAKE, None) == ERANGE
+    assert L.engram_check_inputs(plan, None, None, 0, 0, FAKE, -1, FAKE, None) == ERANGE
