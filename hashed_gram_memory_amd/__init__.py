@@ -32,6 +32,7 @@ _SCALE_FORMATS = {"f32_row": SCALE_F32_ROW, "e8m0_block32": SCALE_E8M0_BLOCK32}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libengram.so")
+MEASURE_LIB_PATH = os.path.join(_HERE, "libengram_measure.so")  # synthetic fill and ceiling probes (not the lookup)
 
 STATUS = {0: "ENGRAM_OK", -1: "ENGRAM_EINVAL", -2: "ENGRAM_ERANGE", -3: "ENGRAM_EWORKSPACE",
           -4: "ENGRAM_EHIP", -5: "ENGRAM_EUNSUPPORTED"}
@@ -81,13 +82,6 @@ def _load():
         "engram_dedup": [P, VP, VP, I64, I64, VP, VP, VP, VP, ctypes.c_size_t, VP],
         "engram_dedup_noalloc": [P, VP, VP, I64, I64, VP, VP, VP, VP],
         "engram_check_inputs": [P, VP, VP, I64, I64, VP, I64, VP, VP],
-        "engram_synth_fill": [VP, VP, U64, U32, U64, VP],
-        "engram_synth_fill_e8m0": [VP, U64, U32, U64, VP],
-        "engram_probe_read": [VP, U64, VP, VP],
-        "engram_probe_copy": [VP, VP, U64, VP],
-        "engram_probe_rows": [P, VP, I64, VP, VP],
-        "engram_probe_random": [VP, U64, U32, U64, U64, VP, VP],
-        "engram_probe_records": [VP, U64, U32, I64, U64, VP, VP],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -99,10 +93,36 @@ def _load():
 
 
 _lib = _load()
+_measure_lib = None
 
 
 def lib() -> ctypes.CDLL:
     return _lib
+
+
+def measure_lib() -> ctypes.CDLL:
+    """libengram_measure.so: the seeded synthetic table fill and the memory-ceiling probes (loaded on first use)."""
+    global _measure_lib
+    if _measure_lib is None:
+        if not os.path.exists(MEASURE_LIB_PATH):
+            raise ImportError(f"{MEASURE_LIB_PATH} is not built; run `python hashed_gram_memory_amd/build.py`")
+        m = ctypes.CDLL(MEASURE_LIB_PATH)
+        P, I64, U64, U32, VP = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p
+        sig = {
+            "engram_synth_fill": [VP, VP, U64, U32, U64, VP],
+            "engram_synth_fill_e8m0": [VP, U64, U32, U64, VP],
+            "engram_probe_read": [VP, U64, VP, VP],
+            "engram_probe_copy": [VP, VP, U64, VP],
+            "engram_probe_rows": [P, VP, I64, VP, VP],
+            "engram_probe_random": [VP, U64, U32, U64, U64, VP, VP],
+            "engram_probe_records": [VP, U64, U32, I64, U64, VP, VP],
+        }
+        for name, args in sig.items():
+            fn = getattr(m, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        _measure_lib = m
+    return _measure_lib
 
 
 def _check(status: int, what: str) -> None:
@@ -467,12 +487,12 @@ def synth_fill(tables, scales, seed: int, stream=None, scale_format: str = "f32_
         if t.dim() != 2 or t.shape[1] != ROW_BYTES or tuple(c.shape) != want:
             raise ValueError(f"sub-table {s}: need table [R, 256] and scales {list(want)}")
         if mx:
-            st = _lib.engram_synth_fill(_dev(t, torch.uint8, "table"), None, t.shape[0], s, seed, _stream(stream))
+            st = measure_lib().engram_synth_fill(_dev(t, torch.uint8, "table"), None, t.shape[0], s, seed, _stream(stream))
             _check(st, "engram_synth_fill")
-            st = _lib.engram_synth_fill_e8m0(_dev(c, torch.uint8, "scales"), t.shape[0], s, seed, _stream(stream))
+            st = measure_lib().engram_synth_fill_e8m0(_dev(c, torch.uint8, "scales"), t.shape[0], s, seed, _stream(stream))
             _check(st, "engram_synth_fill_e8m0")
         else:
-            st = _lib.engram_synth_fill(_dev(t, torch.uint8, "table"), _dev(c, torch.float32, "scales"), t.shape[0],
+            st = measure_lib().engram_synth_fill(_dev(t, torch.uint8, "table"), _dev(c, torch.float32, "scales"), t.shape[0],
                                         s, seed, _stream(stream))
             _check(st, "engram_synth_fill")
 
@@ -486,7 +506,7 @@ def probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     if not src.is_cuda or not src.is_contiguous():
         raise ValueError("src must be a contiguous device tensor")
     nbytes = src.numel() * src.element_size()
-    _check(_lib.engram_probe_read(src.data_ptr(), nbytes - nbytes % 16, _dev(sink, torch.int32, "sink"),
+    _check(measure_lib().engram_probe_read(src.data_ptr(), nbytes - nbytes % 16, _dev(sink, torch.int32, "sink"),
                                   _stream(stream)), "engram_probe_read")
 
 
@@ -495,7 +515,7 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     nbytes = src.numel() * src.element_size()
     if nbytes != dst.numel() * dst.element_size() or not (src.is_cuda and dst.is_cuda):
         raise ValueError("src and dst must be device tensors of the same byte size")
-    _check(_lib.engram_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes - nbytes % 16, _stream(stream)),
+    _check(measure_lib().engram_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes - nbytes % 16, _stream(stream)),
            "engram_probe_copy")
 
 
@@ -504,7 +524,7 @@ def probe_random(buf: torch.Tensor, chunk_bytes: int, read_bytes: int, sink: tor
     """Random reads of whole ``chunk_bytes`` chunks of the contiguous device tensor ``buf`` (engram_probe_random)."""
     if not buf.is_cuda or not buf.is_contiguous():
         raise ValueError("buf must be a contiguous device tensor")
-    _check(_lib.engram_probe_random(buf.data_ptr(), buf.numel() * buf.element_size(), chunk_bytes, read_bytes, seed,
+    _check(measure_lib().engram_probe_random(buf.data_ptr(), buf.numel() * buf.element_size(), chunk_bytes, read_bytes, seed,
                                     _dev(sink, torch.int32, "sink"), _stream(stream)), "engram_probe_random")
 
 
@@ -518,7 +538,7 @@ def probe_records(buf: torch.Tensor, layout: str, out: torch.Tensor, seed: int =
         raise ValueError("buf must be a contiguous device tensor")
     if out.dtype != torch.float32 or out.dim() != 3 or tuple(out.shape[1:]) != (2, 256) or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 [n_tok, 2, 256] tensor")
-    _check(_lib.engram_probe_records(buf.data_ptr(), buf.numel() * buf.element_size(),
+    _check(measure_lib().engram_probe_records(buf.data_ptr(), buf.numel() * buf.element_size(),
                                      PROBE_RECORD_LAYOUTS.index(layout), out.shape[0], seed, out.data_ptr(),
                                      _stream(stream)), "engram_probe_records")
 
@@ -527,6 +547,6 @@ def probe_rows(plan: Plan, addr: torch.Tensor, out: torch.Tensor, stream=None) -
     """The gather without its scale reads (engram_probe_rows)."""
     if addr.dim() != 2 or addr.shape[1] != N_SUB or tuple(out.shape) != (addr.shape[0], N_MODULES, ROW_BYTES):
         raise ValueError("addr must be [n_tok, 48] and out [n_tok, 2, 256]")
-    _check(_lib.engram_probe_rows(plan.handle, _dev(addr, torch.uint32, "addr"), addr.shape[0],
+    _check(measure_lib().engram_probe_rows(plan.handle, _dev(addr, torch.uint32, "addr"), addr.shape[0],
                                   _dev(out, torch.float32, "out"), _stream(stream)), "engram_probe_rows")
     return out

@@ -1,4 +1,4 @@
-"""Build libengram.so (HIP kernels + C ABI) for gfx950 with hipcc.
+"""Build libengram.so (HIP kernels + C ABI) and libengram_measure.so (synthetic fill, probes) for gfx950 with hipcc.
 
 Usage: python hashed_gram_memory_amd/build.py   (run by path: importing the package needs the library)
 Cross-compiles without a GPU.  Object files go to _build/ next to this file.
@@ -19,8 +19,11 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libengram.so")
 DEMO_SRC = os.path.join(CSRC, "examples", "c_abi_demo.c")
 DEMO = os.path.join(HERE, "c_abi_demo")
-SOURCES = ["engram_api.cpp", "hash.hip", "gather_reduce.hip", "dedup.hip", "synth_fill.hip", "probe.hip", "lookup.hip", "gate_io.hip", "gather_batched.hip",
-           "dedup_noalloc.hip", "check.hip"]
+# the lookup library (the product) and the measurement library (synthetic table fill, memory-ceiling probes)
+SOURCES = ["engram_api.cpp", "hash.hip", "gather_reduce.hip", "dedup.hip", "lookup.hip", "gate_io.hip",
+           "gather_batched.hip", "dedup_noalloc.hip", "check.hip"]
+MEASURE_SOURCES = ["synth_fill.hip", "probe.hip"]
+MEASURE_LIB = os.path.join(HERE, "libengram_measure.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
@@ -48,26 +51,32 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    # A plain C consumer of the ABI (host code only), linked against the library just built.
+        raise RuntimeError(f"link of {os.path.basename(out)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + MEASURE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[f] for f in SOURCES], LIB)
+    _link([objs[f] for f in MEASURE_SOURCES], MEASURE_LIB)
+    # A plain C consumer of the ABI (host code only), linked against the libraries just built.
     cmd = ["gcc", "-O2", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I", "/opt/rocm/include", DEMO_SRC,
-           "-o", DEMO + ".tmp", "-L", HERE, "-lengram", "-L", "/opt/rocm/lib", "-lamdhip64",
+           "-o", DEMO + ".tmp", "-L", HERE, "-lengram", "-lengram_measure", "-L", "/opt/rocm/lib", "-lamdhip64",
            "-Wl,-rpath,$ORIGIN", "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"c_abi_demo build failed:\n{r.stdout}\n{r.stderr}")
     os.replace(DEMO + ".tmp", DEMO)
     if verbose:
-        print("built", LIB, "and", DEMO)
+        print("built", LIB, MEASURE_LIB, "and", DEMO)
     return LIB
 
 

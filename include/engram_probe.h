@@ -1,6 +1,6 @@
 /*
  * engram_probe.h -- memory-ceiling probes (measurement only; not part of the
- * lookup).
+ * lookup: these calls live in the measurement library, libengram_measure.so).
  *
  * The lookup's gather is bound by HBM.  These kernels measure, on the same
  * device and in the same process, what the memory system delivers for the

@@ -1,7 +1,8 @@
 /*
  * engram_synth.h -- seeded synthetic tables on the device (input data only).
  *
- * Not part of the lookup.  Full-size Engram tables (48 x 2^24 rows x 256 B,
+ * Not part of the lookup: these calls live in the measurement library,
+ * libengram_measure.so, not in libengram.so.  Full-size Engram tables (48 x 2^24 rows x 256 B,
  * 192 GiB) cannot be shipped from the host in reasonable time, so the
  * synthetic workloads define every table byte and scale by a counter-based
  * generator and fill the tables on the device.  Host code regenerates any

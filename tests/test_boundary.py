@@ -24,20 +24,32 @@ def L(hg):
     return hg.lib()
 
 
-def _declared_functions():
-    names = set()
-    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
-        text = open(h).read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names.update(re.findall(r"\b(engram_\w+)\s*\(", text))
-    return sorted(names)
+def _declared_functions(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(engram_\w+)\s*\(", text)))
 
 
-def test_every_declared_symbol_is_exported(L):
-    names = _declared_functions()
-    assert len(names) >= 10
-    for n in names:
+def test_every_header_is_covered():
+    assert sorted(os.path.basename(h) for h in glob.glob(os.path.join(ROOT, "include", "*.h"))) == [
+        "engram.h", "engram_probe.h", "engram_synth.h"]
+
+
+def test_every_declared_symbol_is_exported(hg, L):
+    """engram.h is the lookup library's; engram_synth.h and engram_probe.h are the measurement library's, and the
+    lookup library exports none of their symbols."""
+    import ctypes as _ct
+    lookup = _declared_functions("engram.h")
+    measure = _declared_functions("engram_synth.h") + _declared_functions("engram_probe.h")
+    assert len(lookup) >= 15 and len(measure) >= 7
+    M = hg.measure_lib()
+    for n in lookup:
         assert hasattr(L, n), n
+    for n in measure:
+        assert hasattr(M, n), n
+    plain = _ct.CDLL(hg.LIB_PATH)
+    for n in measure:
+        assert not hasattr(plain, n), n
 
 
 def _desc(hg, rows=None, tabs=None, scs=None):
@@ -181,12 +193,13 @@ def test_dedup_validation(hg, plan):
 
 
 def test_synth_fill_validation(hg):
+    M = hg.measure_lib()
     L = hg.lib()
-    assert L.engram_synth_fill(FAKE, FAKE, 0, 0, 1, None) == ERANGE
-    assert L.engram_synth_fill(FAKE, FAKE, (1 << 32) + 1, 0, 1, None) == ERANGE
-    assert L.engram_synth_fill(FAKE, FAKE, 16, 48, 1, None) == EINVAL
-    assert L.engram_synth_fill(FAKE + 4, FAKE, 16, 0, 1, None) == EINVAL
-    assert L.engram_synth_fill(FAKE, FAKE + 2, 16, 0, 1, None) == EINVAL
+    assert M.engram_synth_fill(FAKE, FAKE, 0, 0, 1, None) == ERANGE
+    assert M.engram_synth_fill(FAKE, FAKE, (1 << 32) + 1, 0, 1, None) == ERANGE
+    assert M.engram_synth_fill(FAKE, FAKE, 16, 48, 1, None) == EINVAL
+    assert M.engram_synth_fill(FAKE + 4, FAKE, 16, 0, 1, None) == EINVAL
+    assert M.engram_synth_fill(FAKE, FAKE + 2, 16, 0, 1, None) == EINVAL
 
 
 def test_status_strings(hg):
@@ -213,18 +226,19 @@ def test_no_cpu_fallback_in_package():
 
 
 def test_probe_validation(hg, plan):
+    M = hg.measure_lib()
     L = hg.lib()
-    assert L.engram_probe_read(None, 16, FAKE, None) == EINVAL
-    assert L.engram_probe_read(FAKE, 17, FAKE, None) == EINVAL
-    assert L.engram_probe_read(FAKE + 8, 16, FAKE, None) == EINVAL
-    assert L.engram_probe_read(FAKE, 0, FAKE, None) == OK
-    assert L.engram_probe_copy(FAKE, FAKE + 256, 1024, None) == EINVAL  # overlap
-    assert L.engram_probe_copy(FAKE, None, 1024, None) == EINVAL
-    assert L.engram_probe_copy(FAKE, FAKE + 4096, 0, None) == OK
-    assert L.engram_probe_rows(None, FAKE, 1, FAKE, None) == EINVAL
-    assert L.engram_probe_rows(plan, FAKE, -1, FAKE, None) == ERANGE
-    assert L.engram_probe_rows(plan, FAKE, 0, FAKE, None) == OK
-    assert L.engram_probe_rows(plan, FAKE, 1, FAKE + 4, None) == EINVAL
+    assert M.engram_probe_read(None, 16, FAKE, None) == EINVAL
+    assert M.engram_probe_read(FAKE, 17, FAKE, None) == EINVAL
+    assert M.engram_probe_read(FAKE + 8, 16, FAKE, None) == EINVAL
+    assert M.engram_probe_read(FAKE, 0, FAKE, None) == OK
+    assert M.engram_probe_copy(FAKE, FAKE + 256, 1024, None) == EINVAL  # overlap
+    assert M.engram_probe_copy(FAKE, None, 1024, None) == EINVAL
+    assert M.engram_probe_copy(FAKE, FAKE + 4096, 0, None) == OK
+    assert M.engram_probe_rows(None, FAKE, 1, FAKE, None) == EINVAL
+    assert M.engram_probe_rows(plan, FAKE, -1, FAKE, None) == ERANGE
+    assert M.engram_probe_rows(plan, FAKE, 0, FAKE, None) == OK
+    assert M.engram_probe_rows(plan, FAKE, 1, FAKE + 4, None) == EINVAL
 
 
 def test_lookup_validation(hg, plan):
@@ -239,6 +253,7 @@ def test_lookup_validation(hg, plan):
 
 
 def test_plan_scale_formats(hg):
+    M = hg.measure_lib()
     L = hg.lib()
     d, keep = _desc(hg, scs=[FAKE + 8 * s for s in range(48)])
     d.scale_format = 1
@@ -254,10 +269,10 @@ def test_plan_scale_formats(hg):
     d, keep = _desc(hg)
     d.reserved1 = 1
     assert _plan(hg, d)[0] == EINVAL
-    assert L.engram_synth_fill_e8m0(FAKE, 0, 0, 1, None) == ERANGE
-    assert L.engram_synth_fill_e8m0(FAKE + 4, 16, 0, 1, None) == EINVAL
-    assert L.engram_synth_fill_e8m0(FAKE, 16, 48, 1, None) == EINVAL
-    assert L.engram_synth_fill_e8m0(None, 16, 0, 1, None) == EINVAL
+    assert M.engram_synth_fill_e8m0(FAKE, 0, 0, 1, None) == ERANGE
+    assert M.engram_synth_fill_e8m0(FAKE + 4, 16, 0, 1, None) == EINVAL
+    assert M.engram_synth_fill_e8m0(FAKE, 16, 48, 1, None) == EINVAL
+    assert M.engram_synth_fill_e8m0(None, 16, 0, 1, None) == EINVAL
 
 
 def test_gate_io_validation(hg, plan):
@@ -286,23 +301,25 @@ def test_plan_vocab_map(hg):
 
 
 def test_probe_random_validation(hg):
+    M = hg.measure_lib()
     L = hg.lib()
-    assert L.engram_probe_random(None, 1 << 20, 256, 1 << 20, 1, FAKE, None) == EINVAL
-    assert L.engram_probe_random(FAKE + 16, 1 << 20, 256, 1 << 20, 1, FAKE, None) == EINVAL
-    assert L.engram_probe_random(FAKE, 1 << 20, 300, 1 << 20, 1, FAKE, None) == EUNSUPPORTED
-    assert L.engram_probe_random(FAKE, 100, 256, 1 << 20, 1, FAKE, None) == EINVAL
-    assert L.engram_probe_random(FAKE, 1 << 20, 256, 100, 1, FAKE, None) == OK  # less than one wave: nothing to do
+    assert M.engram_probe_random(None, 1 << 20, 256, 1 << 20, 1, FAKE, None) == EINVAL
+    assert M.engram_probe_random(FAKE + 16, 1 << 20, 256, 1 << 20, 1, FAKE, None) == EINVAL
+    assert M.engram_probe_random(FAKE, 1 << 20, 300, 1 << 20, 1, FAKE, None) == EUNSUPPORTED
+    assert M.engram_probe_random(FAKE, 100, 256, 1 << 20, 1, FAKE, None) == EINVAL
+    assert M.engram_probe_random(FAKE, 1 << 20, 256, 100, 1, FAKE, None) == OK  # less than one wave: nothing to do
 
 
 def test_probe_records_validation(hg):
+    M = hg.measure_lib()
     L = hg.lib()
-    assert L.engram_probe_records(None, 1 << 20, 0, 4, 1, FAKE, None) == EINVAL
-    assert L.engram_probe_records(FAKE + 16, 1 << 20, 0, 4, 1, FAKE, None) == EINVAL
-    assert L.engram_probe_records(FAKE, 1 << 20, 0, 4, 1, FAKE + 4, None) == EINVAL
-    assert L.engram_probe_records(FAKE, 1 << 20, 0, -1, 1, FAKE, None) == EINVAL
-    assert L.engram_probe_records(FAKE, 1 << 20, 4, 4, 1, FAKE, None) == EUNSUPPORTED
-    assert L.engram_probe_records(FAKE, 200, 0, 4, 1, FAKE, None) == EINVAL
-    assert L.engram_probe_records(FAKE, 1 << 20, 3, 0, 1, FAKE, None) == OK
+    assert M.engram_probe_records(None, 1 << 20, 0, 4, 1, FAKE, None) == EINVAL
+    assert M.engram_probe_records(FAKE + 16, 1 << 20, 0, 4, 1, FAKE, None) == EINVAL
+    assert M.engram_probe_records(FAKE, 1 << 20, 0, 4, 1, FAKE + 4, None) == EINVAL
+    assert M.engram_probe_records(FAKE, 1 << 20, 0, -1, 1, FAKE, None) == EINVAL
+    assert M.engram_probe_records(FAKE, 1 << 20, 4, 4, 1, FAKE, None) == EUNSUPPORTED
+    assert M.engram_probe_records(FAKE, 200, 0, 4, 1, FAKE, None) == EINVAL
+    assert M.engram_probe_records(FAKE, 1 << 20, 3, 0, 1, FAKE, None) == OK
 
 
 def test_gather_reduce_batched_validation(hg, plan):
