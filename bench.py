@@ -291,12 +291,17 @@ def measure_controls(hg, torch, workloads, plan, w, batches, addr, out, stream, 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=5000,
+                    help="timed steps (5000 on the default workload: about 2 s of GPU work, long enough for a "
+                         "utilisation sampler to see it)")
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-sample", type=int, default=131072,
                     help="tokens of workload 4 in the CPU oracle baseline (0: skip the baseline)")
     ap.add_argument("--cpu-workloads", default="1,2,3,4",
                     help="workloads the CPU oracle baseline times, with 1 process and with all cores")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="hash (and dedup) the next batch on other streams while the current one is gathered, instead "
+                         "of running each step in order on one stream (measured: helps only the dedup step, ~2%%)")
     ap.add_argument("--no-controls", action="store_true",
                     help="skip the uniform-id and cache-flushed control timings of the gather")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -374,63 +379,121 @@ def main(argv=None) -> int:
     out = torch.empty((n_tok, 2, 256), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     groups = ws = None
+
+    def new_groups():
+        return hg.Groups(torch.empty(n_tok, dtype=torch.int32, device=dev),
+                         torch.empty(n_tok + 1, dtype=torch.int32, device=dev),
+                         torch.empty(1, dtype=torch.int32, device=dev))
+
+    # two buffers of addresses (and groups): batch i's lookup inputs live in buffer i % 2
+    addr_bufs = [addr, torch.empty_like(addr)]
+    group_bufs = [None, None]
     if args.dedup:
-        groups = hg.Groups(torch.empty(n_tok, dtype=torch.int32, device=dev),
-                           torch.empty(n_tok + 1, dtype=torch.int32, device=dev),
-                           torch.empty(1, dtype=torch.int32, device=dev))
+        group_bufs = [new_groups(), new_groups()]
+        groups = group_bufs[0]
         ws = torch.empty(hg.dedup_workspace_bytes(plan, n_tok), dtype=torch.uint8, device=dev)
-
-    def hash_phase(i):
-        b = batches[i % len(batches)]
-        hg.hash(plan, b[1], b[2], out=addr, stream=stream)
-
-    def dedup_phase(i):
-        if args.dedup:
-            b = batches[i % len(batches)]
-            hg.dedup(plan, b[1], b[2], workspace=ws, groups=groups, stream=stream)
+    s_hash = torch.cuda.Stream()  # default priority
+    s_dedup = torch.cuda.Stream() if args.dedup else None
 
     # a batch of sequences is gathered in the batch order (engram_gather_reduce_batched): same results, and
     # sequences that share a prefix read it from L2
     batched = not args.dedup and w.n_seq > 1
 
-    def gather(stream=None):
+    def gather_into(k, stream=None):
         if batched:
-            hg.gather_reduce_batched(plan, addr, w.n_seq, out=out, stream=stream)
+            hg.gather_reduce_batched(plan, addr_bufs[k], w.n_seq, out=out, stream=stream)
         else:
-            hg.gather_reduce(plan, addr, out=out, groups=groups, stream=stream)
+            hg.gather_reduce(plan, addr_bufs[k], out=out, groups=group_bufs[k], stream=stream)
 
-    def gather_phase():
-        gather(stream)
+    def gather(stream=None):
+        gather_into(0, stream)
 
-    def step(i):
-        hash_phase(i)
-        dedup_phase(i)
-        gather_phase()
-
-    _log(f"warmup {args.warmup}")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     flush = torch.ones(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib > 0 else None
     flush_sink = torch.zeros((), dtype=torch.uint8, device=dev)
-    _log(f"timing {args.steps} steps")
+
+    def run_steps(n: int, pipelined: bool, ev=None) -> None:
+        """n steps.  Step i hashes (and groups) batch i into buffer i % 2, then gathers that buffer.  Pipelined, the
+        hash and dedup of batch i + 1 run on side streams while batch i is gathered -- they depend on the ids
+        alone -- and wait only for the gather that last read their buffer; serial, everything runs in order on one
+        stream.  ev[i] = 6 events around step i's hash, dedup and gather."""
+        freed = [torch.cuda.Event(), torch.cuda.Event()]  # the gather that last read buffer k has finished
+
+        def produce(i):
+            k, b = i % 2, batches[i % len(batches)]
+            hs = s_hash if pipelined else stream
+            if pipelined:
+                hs.wait_event(freed[k])
+            if ev:
+                ev[i][0].record(hs)
+            hg.hash(plan, b[1], b[2], out=addr_bufs[k], stream=hs)
+            if ev:
+                ev[i][1].record(hs)
+            done = []
+            if pipelined:
+                done.append(torch.cuda.Event())
+                done[-1].record(hs)
+            if args.dedup:
+                ds = s_dedup if pipelined else stream
+                if pipelined:
+                    ds.wait_event(freed[k])
+                if ev:
+                    ev[i][2].record(ds)
+                hg.dedup(plan, b[1], b[2], workspace=ws, groups=group_bufs[k], stream=ds)
+                if ev:
+                    ev[i][3].record(ds)
+                if pipelined:
+                    done.append(torch.cuda.Event())
+                    done[-1].record(ds)
+            return done
+
+        def consume(i, done):
+            k = i % 2
+            for e in done:
+                stream.wait_event(e)
+            if flush is not None:
+                flush_sink.copy_(flush.max())
+            if ev:
+                ev[i][4].record(stream)
+            gather_into(k, stream)
+            if ev:
+                ev[i][5].record(stream)
+            if pipelined:
+                freed[k].record(stream)
+
+        if pipelined:
+            done = produce(0)
+            for i in range(n):
+                consume(i, done)
+                if i + 1 < n:
+                    done = produce(i + 1)
+        else:
+            for i in range(n):
+                consume(i, produce(i))
+
+    pipelined = args.pipeline
+    _log(f"warmup {args.warmup}")
+    run_steps(args.warmup, pipelined)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    _log(f"timing {args.steps} steps ({'pipelined' if pipelined else 'serial'})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        e = ev[i]
-        if flush is not None:
-            flush_sink.copy_(flush.max())
-        e[0].record(stream)
-        hash_phase(i)
-        e[1].record(stream)
-        dedup_phase(i)
-        e[2].record(stream)
-        gather_phase()
-        e[3].record(stream)
+    run_steps(args.steps, pipelined, ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    serial = None
+    if pipelined:
+        # the same steps one after the other on one stream, for comparison with the pipelined ones
+        n_serial = min(args.steps, 200)
+        run_steps(min(args.warmup, 5), False)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        run_steps(n_serial, False)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t1) / n_serial
+        serial = {"steps": n_serial, "us_per_step": dt * 1e6, "tokens_per_s": n_tok / dt}
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -523,8 +586,8 @@ def main(argv=None) -> int:
     distinct = int(np.unique(keys).size)
 
     hash_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    dedup_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if args.dedup else None
-    gather_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    dedup_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) if args.dedup else None
+    gather_ms = float(np.mean([e[4].elapsed_time(e[5]) for e in ev]))
     ms_per_step = wall / args.steps * 1e3
     tok_s = n_tok / (ms_per_step / 1e3)
     n_unique = int(groups.n_unique.item()) if args.dedup else None
@@ -569,9 +632,11 @@ def main(argv=None) -> int:
             "ids": "uniform over 129280 (control)" if args.uniform_ids else "Zipf(1.1) over 129280",
             "flush_mib_per_step": args.flush_mib,
             "id_batches": args.id_batches,
-            "step": "engram_hash + engram_dedup + engram_gather_reduce (dedup mode)" if args.dedup
-                    else "engram_hash + engram_gather_reduce_batched" if batched
-                    else "engram_hash + engram_gather_reduce",
+            "step": ("engram_hash + engram_dedup + engram_gather_reduce (dedup mode)" if args.dedup
+                     else "engram_hash + engram_gather_reduce_batched" if batched
+                     else "engram_hash + engram_gather_reduce")
+                    + ("; batch i+1's hash (and dedup) on other streams while batch i is gathered" if pipelined
+                       else "; all in order on one stream"),
             "n_unique": n_unique,
         },
         "roofline": {
@@ -593,6 +658,7 @@ def main(argv=None) -> int:
                     "each 64-byte scale request as 128 bytes",
         },
         "controls": controls,
+        "serial_step": serial,
         "per_step_us": {"eager": ms_per_step * 1e3,
                         "graph_two_call": None if graph is None else graph["two_call_us_per_step"],
                         "graph_fused": None if graph is None else graph["fused_us_per_step"]},

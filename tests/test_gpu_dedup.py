@@ -212,3 +212,16 @@ def test_dedup_vocab_bounds_of_compaction(vocab):
     groups = lib().dedup(plan, *to_dev_ids(ids, hist))
     torch.cuda.synchronize()
     _check_groups(groups, ids, hist)
+
+
+def test_dedup_at_the_token_limit():
+    """2^22 tokens, the most one call takes (1,024 tiles: every pass tile sums up to 1,023 earlier tiles' counts in
+    16 rounds of loads per thread column), ids uniform over a 129,280-id vocabulary (17-bit compacted keys)."""
+    n_seq, seq_len = 4, 1 << 20
+    _say(f"dedup {n_seq} x {seq_len} tokens (the per-call limit)")
+    rng = np.random.default_rng(22)
+    ids = rng.integers(0, 129280, size=(n_seq, seq_len), dtype=np.int64).astype(np.int32)
+    plan = dummy_plan(4096, 129280)
+    groups = lib().dedup(plan, *to_dev_ids(ids, None))
+    torch.cuda.synchronize()
+    _check_groups(groups, ids, None)
