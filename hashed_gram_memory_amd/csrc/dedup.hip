@@ -55,6 +55,8 @@
 //           the last one needed writes the token order into the caller's perm
 //   groups  flags where the key changes, a look-back scan of their counts,
 //           offsets and the group count
+#include <stdlib.h>
+
 #include <algorithm>
 
 #include "engram_internal.h"
@@ -75,7 +77,7 @@ constexpr uint32_t kCompactMin = 1u << 16;  // compaction for vocabularies above
 constexpr uint32_t kCompactMax = 1u << 18;  // ... up to this
 constexpr uint32_t kRankIds = 4096;        // ids per block of the presence bitmap (64 words)
 constexpr uint32_t kMaxBitmapBlocks = kCompactMax / kRankIds;  // 64
-constexpr uint32_t kSpinLimit = 1u << 18;  // waits of about 2^18 x 128 clocks (~14 ms) at most
+constexpr uint32_t kSpinLimit = 1u << 18;  // default bound on a wait: about 2^18 x 128 clocks (~14 ms)
 
 // Status words.  A pass tile publishes its 256 digit counts (each < 2^15)
 // as 128 words of two 16-bit halves, each half with its top bit set; a
@@ -94,7 +96,8 @@ struct Ctl {
     uint32_t has_hi;    // keys wider than 64 bits
     uint32_t bits;      // B
     uint32_t n_ids;     // D (compaction) or 0
-    uint32_t pad0[59];
+    uint32_t spin_limit;  // bound on the polls of one wait (set by init each call)
+    uint32_t pad0[58];
     // modified with atomics during the call
     uint32_t tile_ctr[kMaxPasses + 1];  // tile tickets of each pass, and of the group kernel
     uint32_t error;                     // a look-back gave up
@@ -150,10 +153,11 @@ __host__ __device__ inline uint32_t bits_for(uint64_t count) {  // smallest B >=
 
 // Wait until a published status word is ready; bounded.  Returns the word,
 // or 0 after recording an error when the wait gives up.
-__device__ __forceinline__ uint32_t wait_ready(const uint32_t* p, uint32_t word, uint32_t ready, uint32_t* error) {
+__device__ __forceinline__ uint32_t wait_ready(const uint32_t* p, uint32_t word, uint32_t ready, uint32_t* error,
+                                               uint32_t limit) {
     uint32_t spins = 0;
     while ((word & ready) != ready) {
-        if (++spins > kSpinLimit || load_status(error) != 0u) {
+        if (++spins > limit || load_status(error) != 0u) {
             store_status(error, 1u);
             return 0u;
         }
@@ -252,11 +256,14 @@ size_t layout(uint32_t n, uint32_t vocab, char* base, Workspace* w) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void init_kernel(Ids s, uint32_t n, uint32_t vocab, uint32_t compact,
                                                    uint32_t zero_words, Workspace w, uint32_t id_bits,
-                                                   uint32_t id_passes, uint32_t id_hi) {
+                                                   uint32_t id_passes, uint32_t id_hi, uint32_t spin_limit) {
     const uint32_t gtid = blockIdx.x * 256u + threadIdx.x;
     const uint32_t stride = gridDim.x * 256u;
     if (gtid <= kMaxPasses) w.ctl->tile_ctr[gtid] = 0u;
-    if (gtid == 0) w.ctl->error = 0u;
+    if (gtid == 0) {
+        w.ctl->error = 0u;
+        w.ctl->spin_limit = spin_limit;
+    }
     for (uint32_t i = gtid; i < zero_words; i += stride) w.hist[i] = 0u;  // histograms and statuses
     if (gtid == 0 && !compact) {
         w.ctl->bits = id_bits;
@@ -453,6 +460,7 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
     if (static_cast<uint32_t>(pass) >= npass) return;  // this call's keys need fewer passes
     const bool has_hi = ctl->has_hi != 0u;
     const bool last = static_cast<uint32_t>(pass) + 1u == npass;
+    const uint32_t limit = ctl->spin_limit;
 
     __shared__ uint32_t s_tile;
     __shared__ uint32_t wave_hist[kPassWaves][kRadix];  // counts per wave, then exclusive prefixes across waves
@@ -554,7 +562,7 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
             for (uint32_t j = 0; j < 8; ++j) {
                 const uint32_t t = t0 + j * kGroupsOfRows;
                 if (t < tile) {
-                    const uint32_t c = wait_ready(counts + size_t(t) * kStatusWords + i, v[j], kPairReady, &ctl->error);
+                    const uint32_t c = wait_ready(counts + size_t(t) * kStatusWords + i, v[j], kPairReady, &ctl->error, limit);
                     sum_lo += c & 0x7FFFu;
                     sum_hi += (c >> 16) & 0x7FFFu;
                 }
@@ -623,6 +631,7 @@ __global__ __launch_bounds__(kPassThreads) void groups_kernel(uint32_t n, uint32
     __syncthreads();
     const uint32_t tile = s_tile;
     const uint32_t q = ctl->npass & 1u;  // buffer the last pass wrote
+    const uint32_t limit = ctl->spin_limit;
     const bool has_hi = ctl->has_hi != 0u;
     const uint64_t* __restrict__ lo = w.lo[q];
     const uint64_t* __restrict__ hi = w.hi[q];
@@ -648,7 +657,7 @@ __global__ __launch_bounds__(kPassThreads) void groups_kernel(uint32_t n, uint32
         uint32_t acc = 0;  // groups in the earlier tiles, lane by lane
         for (uint32_t t0 = 0; t0 < tile; t0 += 64u) {
             const uint32_t t = t0 + lane;
-            if (t < tile) acc += wait_ready(st + t, load_status(st + t), kWordReady, &ctl->error) & ~kWordReady;
+            if (t < tile) acc += wait_ready(st + t, load_status(st + t), kWordReady, &ctl->error, limit) & ~kWordReady;
         }
         const uint32_t excl = wave_sum(acc);
         if (lane == 0) {
@@ -685,6 +694,16 @@ __global__ void empty_kernel(int32_t* __restrict__ offsets, int32_t* __restrict_
 
 }  // namespace
 
+// Bound on the polls of one device-side wait: ENGRAM_DEDUP_SPIN_LIMIT from the environment when set (a test forces
+// the give-up path with a small value), else kSpinLimit.
+static uint32_t dedup_spin_limit() {
+    const char* v = getenv("ENGRAM_DEDUP_SPIN_LIMIT");
+    if (!v || !*v) return kSpinLimit;
+    char* end = nullptr;
+    const unsigned long x = strtoul(v, &end, 10);
+    return (end && *end == '\0' && x <= 0xFFFFFFFFul) ? static_cast<uint32_t>(x) : kSpinLimit;
+}
+
 size_t dedup_workspace_bytes(uint32_t n, uint32_t vocab_size) {
     return n == 0 ? 0 : layout(n, vocab_size, nullptr, nullptr);
 }
@@ -705,7 +724,7 @@ hipError_t launch_dedup(const int32_t* ids, const int32_t* history, uint32_t n, 
     const uint32_t zero_words = static_cast<uint32_t>(zero_bytes / sizeof(uint32_t));
     const uint32_t init_blocks = std::min<uint32_t>(2048u, (std::max<uint32_t>(n, zero_words) + 255u) / 256u);
     hipLaunchKernelGGL(init_kernel, dim3(init_blocks), dim3(256), 0, stream, s, n, vocab_size, uint32_t(k.compact),
-                       zero_words, w, k.bits, uint32_t(k.max_passes), uint32_t(k.hi_possible));
+                       zero_words, w, k.bits, uint32_t(k.max_passes), uint32_t(k.hi_possible), dedup_spin_limit());
     if (k.compact)
         hipLaunchKernelGGL(bitmap_kernel, dim3((vocab_size + kRankIds - 1u) / kRankIds), dim3(256), 0, stream,
                            vocab_size, w);

@@ -320,6 +320,9 @@ int engram_dedup_workspace(engram_plan_t plan, int64_t n_tok, size_t* bytes);
  *             happen unless the device stalls a running workgroup for
  *             milliseconds): perm and offsets are then invalid, and
  *             engram_gather_reduce in dedup mode treats the groups as empty.
+ *             The bound is 262,144 polls per wait; the environment variable
+ *             ENGRAM_DEDUP_SPIN_LIMIT, read at each call, overrides it (a
+ *             test forces the give-up path with a small value).
  *   ws        device workspace of ws_bytes >= engram_dedup_workspace(plan,
  *             n_tok), 256-byte aligned, owned by the caller.  It keeps a
  *             small state between calls (no clearing needed, initial

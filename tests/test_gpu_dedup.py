@@ -225,3 +225,41 @@ def test_dedup_at_the_token_limit():
     groups = lib().dedup(plan, *to_dev_ids(ids, None))
     torch.cuda.synchronize()
     _check_groups(groups, ids, None)
+
+
+def test_dedup_gives_up_safely_when_a_wait_is_cut_short(monkeypatch):
+    """With the wait bound forced to 0 polls (ENGRAM_DEDUP_SPIN_LIMIT), a tile that finds an earlier tile's counts
+    not yet published gives up at once.  The call then reports n_unique = -1 and the dedup-mode gather writes
+    nothing, or, if no tile had to wait, the result is exact; every kernel exits normally either way.  A call
+    with the normal bound on the same workspace is exact again."""
+    _say("dedup with the wait bound forced to 0")
+    R = 1024
+    host_t, host_c = workloads.dense_tables(79, R)
+    t, c = small_device_tables(host_t, host_c)
+    plan = lib().Plan(t, c, vocab_size=129280)
+    rng = np.random.default_rng(80)
+    ids = rng.integers(0, 129280, size=(8, 40000)).astype(np.int32)  # 80 tiles per pass
+    d_ids, _ = to_dev_ids(ids, None)
+    n_tok = ids.size
+    ws = torch.empty(lib().dedup_workspace_bytes(plan, n_tok), dtype=torch.uint8, device="cuda")
+    addr = lib().hash(plan, d_ids)
+    direct = lib().gather_reduce(plan, addr)
+    gave_up = 0
+    for rep in range(3):
+        monkeypatch.setenv("ENGRAM_DEDUP_SPIN_LIMIT", "0")
+        groups = lib().dedup(plan, d_ids, workspace=ws)
+        monkeypatch.delenv("ENGRAM_DEDUP_SPIN_LIMIT")
+        out = torch.full_like(direct, float("nan"))
+        lib().gather_reduce(plan, addr, out=out, groups=groups)
+        torch.cuda.synchronize()
+        nu = int(groups.n_unique.item())
+        if nu == -1:
+            gave_up += 1
+            assert bool(torch.isnan(out).all())
+        else:
+            _check_groups(groups, ids, None)
+            assert torch.equal(out, direct)
+    _say(f"gave up in {gave_up} of 3 calls")
+    groups = lib().dedup(plan, d_ids, workspace=ws)
+    torch.cuda.synchronize()
+    _check_groups(groups, ids, None)
