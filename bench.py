@@ -174,7 +174,7 @@ def cpu_baseline(keys, workers: int, tokens4: int) -> dict:
         ids, hist = workloads.make_ids(w)
         if key == 4:
             ids = np.ascontiguousarray(ids[:, :tokens4])
-        _log(f"cpu baseline: oracle on workload {key} ({ids.size} tokens), 1 and {workers} processes")
+        _log(f"cpu baseline: oracle on the {w.name} workload ({ids.size} tokens), 1 and {workers} processes")
         one = _time_oracle(ids, hist, w.rows, w.table_seed, 1)
         many = _time_oracle(ids, hist, w.rows, w.table_seed, workers)
         per[str(key)] = {"tokens": int(ids.size), "rows_per_subtable": w.rows, "cores_1": one, "cores_all": many}
@@ -296,9 +296,11 @@ def main(argv=None) -> int:
                          "utilisation sampler to see it)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-sample", type=int, default=131072,
-                    help="tokens of workload 4 in the CPU oracle baseline (0: skip the baseline)")
+                    help="tokens of the full workload (1 x 131,072 tokens, 2^24-row tables) the CPU oracle baseline takes "
+                         "(0: skip the baseline)")
     ap.add_argument("--cpu-workloads", default="1,2,3,4",
-                    help="workloads the CPU oracle baseline times, with 1 process and with all cores")
+                    help="workload keys (1 tiny, 2 decode, 3 prefill, 4 full) the CPU oracle baseline times, with 1 process "
+                         "and with all cores")
     ap.add_argument("--pipeline", action="store_true",
                     help="hash (and dedup) the next batch on other streams while the current one is gathered, instead "
                          "of running each step in order on one stream (measured: helps only the dedup step, ~2%%)")
@@ -307,7 +309,7 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
-                    help="synthetic workload (4: the full-size prefill the metric is quoted on)")
+                    help="synthetic workload: 1 tiny (512 tokens), 2 decode (64 x 1), 3 prefill (32,768), 4 full (131,072 tokens over 48 x 2^24-row tables, the default), 5 batched (64 x 8,192 sharing a 4,096-token prefix)")
     ap.add_argument("--dedup", action="store_true", help="batched workloads: engram_dedup + dedup-mode gather")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the memory-ceiling probes")
     ap.add_argument("--scale-format", default="f32_row", choices=["f32_row", "e8m0_block32"],
@@ -331,7 +333,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the lookup needs no collective and this build runs on a "
+        print("bench.py measures one GPU only: the lookup needs no collective and the library runs on a "
               "single MI355X; multi-GPU sharding is described in the design notes, not run.", file=sys.stderr)
         return 2
 

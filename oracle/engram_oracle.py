@@ -76,7 +76,7 @@ def sub_index(m: int, n: int, h: int) -> int:
 
 
 # ---------------------------------------------------------------------------
-# Step a1: the id window of each token
+# The id window of each token
 # ---------------------------------------------------------------------------
 
 def windows(ids, history=None, vocab_map=None) -> np.ndarray:
@@ -110,7 +110,7 @@ def windows(ids, history=None, vocab_map=None) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# Step a2: hash, 48 addresses per token
+# Hash: 48 addresses per token
 # ---------------------------------------------------------------------------
 
 def splitmix64(seed: int, count: int) -> list[int]:
@@ -138,7 +138,8 @@ def hash_addresses(win: np.ndarray, mult: np.ndarray, rows) -> np.ndarray:
 
     Eight heads per order and module, one row per (order, head) pair, each
     taken in its own bucket range of R_s rows [GUIDE "Engram"; VRAM].  The
-    multiply-xor form and the modulus are this build's reading.
+    multiply-xor form and the modulus are this oracle's reading, which the
+    library follows.
     """
     win = np.asarray(win, dtype=np.int64)
     rows = [int(r) for r in rows]
@@ -158,7 +159,7 @@ def hash_addresses(win: np.ndarray, mult: np.ndarray, rows) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# Step a4: FP8 E4M3 decode
+# FP8 E4M3 decode
 # ---------------------------------------------------------------------------
 
 def e4m3_value(code: int) -> float:
@@ -191,7 +192,7 @@ BLOCK = 32  # elements per E8M0 scale
 
 
 # ---------------------------------------------------------------------------
-# Steps a3-a5: gather, dequantise, per-module sum
+# Gather, dequantise, per-module sum
 # ---------------------------------------------------------------------------
 
 def row_scales(scales_s, a, scale_format: str) -> np.ndarray:
@@ -222,10 +223,10 @@ def gather_reduce(tables, scales, addr, scale_format: str = "f32_row") -> tuple[
         for q in range(ROWS_PER_MODULE):
             s = ROWS_PER_MODULE * m + q
             a = addr[:, s].astype(np.int64)
-            codes = np.asarray(tables[s])[a]                           # a3: [n_tok, 256] bytes
-            sc = row_scales(scales[s], a, scale_format)                 # a3: [n_tok, 256]
-            terms = E4M3_TABLE[codes] * sc                              # a4
-            out[:, m, :] += terms                                       # a5
+            codes = np.asarray(tables[s])[a]                           # gather: [n_tok, 256] bytes
+            sc = row_scales(scales[s], a, scale_format)                 # gather: [n_tok, 256]
+            terms = E4M3_TABLE[codes] * sc                              # dequantise
+            out[:, m, :] += terms                                       # per-module sum
             abs_sum[:, m, :] += np.abs(terms)
     return out, abs_sum
 
@@ -264,7 +265,7 @@ def lookup(ids, history, tables, scales, rows, hash_seed: int = DEFAULT_HASH_SEE
 
 
 # ---------------------------------------------------------------------------
-# Step a6: deduplication of equal windows
+# Deduplication of equal windows
 # ---------------------------------------------------------------------------
 
 def dedup(win: np.ndarray) -> tuple[np.ndarray, np.ndarray, int]:
