@@ -310,7 +310,10 @@ def main(argv=None) -> int:
                     help="after the timed region, run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5],
                     help="synthetic workload: 1 tiny (512 tokens), 2 decode (64 x 1), 3 prefill (32,768), 4 full (131,072 tokens over 48 x 2^24-row tables, the default), 5 batched (64 x 8,192 sharing a 4,096-token prefix)")
-    ap.add_argument("--dedup", action="store_true", help="batched workloads: engram_dedup + dedup-mode gather")
+    ap.add_argument("--dedup", action="store_true",
+                    help="batched workloads: engram_dedup + engram_lookup_dedup (one hash and gather per group)")
+    ap.add_argument("--dedup-two-call", action="store_true",
+                    help="with --dedup: engram_hash + engram_dedup + engram_gather_reduce in dedup mode instead")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the memory-ceiling probes")
     ap.add_argument("--scale-format", default="f32_row", choices=["f32_row", "e8m0_block32"],
                     help="row scales: one fp32 per row, or 8 E8M0 bytes per row (one per 32 elements)")
@@ -400,10 +403,15 @@ def main(argv=None) -> int:
     # a batch of sequences is gathered in the batch order (engram_gather_reduce_batched): same results, and
     # sequences that share a prefix read it from L2
     batched = not args.dedup and w.n_seq > 1
+    # dedup step: the fused lookup over the groups (no address buffer, no hash launch), or hash + dedup-mode gather
+    fused_dedup = args.dedup and not args.dedup_two_call
 
-    def gather_into(k, stream=None):
+    def gather_into(k, stream=None, b=None):
         if batched:
             hg.gather_reduce_batched(plan, addr_bufs[k], w.n_seq, out=out, stream=stream)
+        elif fused_dedup:
+            b = batches[0] if b is None else b
+            hg.lookup(plan, b[1], b[2], out=out, groups=group_bufs[k], stream=stream)
         else:
             hg.gather_reduce(plan, addr_bufs[k], out=out, groups=group_bufs[k], stream=stream)
 
@@ -425,15 +433,16 @@ def main(argv=None) -> int:
             hs = s_hash if pipelined else stream
             if pipelined:
                 hs.wait_event(freed[k])
-            if ev:
-                ev[i][0].record(hs)
-            hg.hash(plan, b[1], b[2], out=addr_bufs[k], stream=hs)
-            if ev:
-                ev[i][1].record(hs)
             done = []
-            if pipelined:
-                done.append(torch.cuda.Event())
-                done[-1].record(hs)
+            if not fused_dedup:
+                if ev:
+                    ev[i][0].record(hs)
+                hg.hash(plan, b[1], b[2], out=addr_bufs[k], stream=hs)
+                if ev:
+                    ev[i][1].record(hs)
+                if pipelined:
+                    done.append(torch.cuda.Event())
+                    done[-1].record(hs)
             if args.dedup:
                 ds = s_dedup if pipelined else stream
                 if pipelined:
@@ -449,14 +458,14 @@ def main(argv=None) -> int:
             return done
 
         def consume(i, done):
-            k = i % 2
+            k, b = i % 2, batches[i % len(batches)]
             for e in done:
                 stream.wait_event(e)
             if flush is not None:
                 flush_sink.copy_(flush.max())
             if ev:
                 ev[i][4].record(stream)
-            gather_into(k, stream)
+            gather_into(k, stream, b)
             if ev:
                 ev[i][5].record(stream)
             if pipelined:
@@ -587,16 +596,17 @@ def main(argv=None) -> int:
     keys |= np.arange(48, dtype=np.uint64)[None, :] << np.uint64(32)
     distinct = int(np.unique(keys).size)
 
-    hash_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    hash_ms = None if fused_dedup else float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     dedup_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) if args.dedup else None
     gather_ms = float(np.mean([e[4].elapsed_time(e[5]) for e in ev]))
     ms_per_step = wall / args.steps * 1e3
     tok_s = n_tok / (ms_per_step / 1e3)
     n_unique = int(groups.n_unique.item()) if args.dedup else None
     if args.dedup:
-        # one lookup per group (rows, scales, addresses, its offsets pair) + one perm read and one
-        # 2 KiB output store per token
-        gather_bytes = n_unique * (48 * 256 + scale_bytes + 48 * 4 + 8) + n_tok * (4 + 2 * 256 * 4)
+        # one lookup per group (rows, scales, its offsets pair, and either its 48 addresses or, fused, its 4 window
+        # ids) + one perm read and one 2 KiB output store per token
+        per_group = 48 * 256 + scale_bytes + 8 + (4 * 4 if fused_dedup else 48 * 4)
+        gather_bytes = n_unique * per_group + n_tok * (4 + 2 * 256 * 4)
     else:
         gather_bytes = (GATHER_BYTES_PER_TOKEN - 48 * 4 + scale_bytes) * n_tok
     achieved = gather_bytes / (gather_ms / 1e3) / 1e9
@@ -634,7 +644,8 @@ def main(argv=None) -> int:
             "ids": "uniform over 129280 (control)" if args.uniform_ids else "Zipf(1.1) over 129280",
             "flush_mib_per_step": args.flush_mib,
             "id_batches": args.id_batches,
-            "step": ("engram_hash + engram_dedup + engram_gather_reduce (dedup mode)" if args.dedup
+            "step": ("engram_dedup + engram_lookup_dedup" if fused_dedup
+                     else "engram_hash + engram_dedup + engram_gather_reduce (dedup mode)" if args.dedup
                      else "engram_hash + engram_gather_reduce_batched" if batched
                      else "engram_hash + engram_gather_reduce")
                     + ("; batch i+1's hash (and dedup) on other streams while batch i is gathered" if pipelined
@@ -643,7 +654,8 @@ def main(argv=None) -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gather_batched_kernel" if batched else "gather_reduce_kernel",
+            "kernel": ("gather_batched_kernel" if batched else "lookup_kernel (dedup mode)" if fused_dedup
+                       else "gather_reduce_kernel"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -668,7 +680,7 @@ def main(argv=None) -> int:
         "hash_ms": hash_ms,
         "dedup_ms": dedup_ms,
         "us_per_step": ms_per_step * 1e3,
-        "hash_gbps": HASH_BYTES_PER_TOKEN * n_tok / (hash_ms / 1e3) / 1e9,
+        "hash_gbps": None if hash_ms is None else HASH_BYTES_PER_TOKEN * n_tok / (hash_ms / 1e3) / 1e9,
         "gather_bytes_per_launch": gather_bytes,
         "unique_rows": {
             "distinct_rows": distinct,

@@ -75,6 +75,7 @@ def _load():
         "engram_hash": [P, VP, VP, I64, I64, VP, VP],
         "engram_gather_reduce": [P, VP, I64, VP, VP, VP, VP, VP],
         "engram_lookup": [P, VP, VP, I64, I64, VP, VP],
+        "engram_lookup_dedup": [P, VP, VP, I64, I64, VP, VP, VP, VP, VP],
         "engram_gather_reduce_batched": [P, VP, I64, I64, VP, VP],
         "engram_gather_weighted": [P, VP, I64, VP, VP, VP],
         "engram_gather_rows": [P, VP, I64, VP, VP],
@@ -320,18 +321,27 @@ def gather_reduce(plan: Plan, addr: torch.Tensor, out: torch.Tensor | None = Non
 
 
 def lookup(plan: Plan, ids: torch.Tensor, history: torch.Tensor | None = None, out: torch.Tensor | None = None,
-           stream=None) -> torch.Tensor:
-    """Hash and gather-reduce in one launch: fp32 [n_seq*seq_len, 2, 256] (engram_lookup)."""
+           groups: Groups | None = None, stream=None) -> torch.Tensor:
+    """Hash and gather-reduce in one launch: fp32 [n_seq*seq_len, 2, 256] (engram_lookup).  With ``groups`` from
+    dedup() of the same ids: one hash and gather per group, the same result (engram_lookup_dedup)."""
     n_seq, seq_len = _ids_shape(ids, history)
     n_tok = n_seq * seq_len
     if out is None:
         out = torch.empty((n_tok, N_MODULES, ROW_BYTES), dtype=torch.float32, device=ids.device)
     elif tuple(out.shape) != (n_tok, N_MODULES, ROW_BYTES):
         raise ValueError("out must be [n_tok, 2, 256]")
-    st = _lib.engram_lookup(plan.handle, _dev(ids, torch.int32, "ids"),
-                            None if history is None else _dev(history, torch.int32, "history"), n_seq, seq_len,
-                            _dev(out, torch.float32, "out"), _stream(stream))
-    _check(st, "engram_lookup")
+    hist = None if history is None else _dev(history, torch.int32, "history")
+    if groups is None:
+        st = _lib.engram_lookup(plan.handle, _dev(ids, torch.int32, "ids"), hist, n_seq, seq_len,
+                                _dev(out, torch.float32, "out"), _stream(stream))
+        _check(st, "engram_lookup")
+        return out
+    _check_groups(groups, n_tok)
+    st = _lib.engram_lookup_dedup(plan.handle, _dev(ids, torch.int32, "ids"), hist, n_seq, seq_len,
+                                  _dev(groups.perm, torch.int32, "perm"), _dev(groups.offsets, torch.int32, "offsets"),
+                                  _dev(groups.n_unique, torch.int32, "n_unique"), _dev(out, torch.float32, "out"),
+                                  _stream(stream))
+    _check(st, "engram_lookup_dedup")
     return out
 
 

@@ -150,8 +150,25 @@ int engram_lookup(engram_plan_t p, const int32_t* ids, const int32_t* history, i
     if (n_tok == 0) return ENGRAM_OK;
     if (!ids || !out || !aligned(ids, 4) || !aligned(out, 16)) return ENGRAM_EINVAL;
     if (history && !aligned(history, 4)) return ENGRAM_EINVAL;
-    hipError_t e = launch_lookup(p->hash, p->gather, ids, history, uint32_t(n_tok), uint32_t(seq_len), out,
-                                 static_cast<hipStream_t>(stream));
+    hipError_t e = launch_lookup(p->hash, p->gather, ids, history, uint32_t(n_tok), uint32_t(seq_len), nullptr,
+                                 nullptr, nullptr, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
+}
+
+int engram_lookup_dedup(engram_plan_t p, const int32_t* ids, const int32_t* history, int64_t n_seq, int64_t seq_len,
+                        const int32_t* perm, const int32_t* offsets, const int32_t* n_unique, float* out,
+                        void* stream) {
+    if (!valid_plan(p)) return ENGRAM_EINVAL;
+    int64_t n_tok = 0;
+    int st = check_tokens(n_seq, seq_len, &n_tok);
+    if (st != ENGRAM_OK) return st;
+    if (n_tok == 0) return ENGRAM_OK;
+    if (!ids || !out || !aligned(ids, 4) || !aligned(out, 16)) return ENGRAM_EINVAL;
+    if (history && !aligned(history, 4)) return ENGRAM_EINVAL;
+    if (!perm || !offsets || !n_unique || !aligned(perm, 4) || !aligned(offsets, 4) || !aligned(n_unique, 4))
+        return ENGRAM_EINVAL;
+    hipError_t e = launch_lookup(p->hash, p->gather, ids, history, uint32_t(n_tok), uint32_t(seq_len), perm, offsets,
+                                 n_unique, out, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
 }
 

@@ -66,8 +66,10 @@ hipError_t launch_gather_reduce(const GatherParams& p, const uint32_t* addr, uin
                                 const int32_t* perm, const int32_t* offsets, const int32_t* n_unique,
                                 float* out, hipStream_t stream);
 
+// perm == nullptr: direct mode; else dedup mode with engram_dedup's groups.
 hipError_t launch_lookup(const HashParams& h, const GatherParams& g, const int32_t* ids, const int32_t* history,
-                         uint32_t n_tok, uint32_t seq_len, float* out, hipStream_t stream);
+                         uint32_t n_tok, uint32_t seq_len, const int32_t* perm, const int32_t* offsets,
+                         const int32_t* n_unique, float* out, hipStream_t stream);
 
 // weights != nullptr: weighted per-module sums into out [n_tok][2][256];
 // weights == nullptr: un-reduced rows into out [n_tok][48][256].

@@ -18,6 +18,12 @@
 // accumulation is the fused multiply-add sequence of gather_reduce_kernel, so
 // the result is bitwise identical to engram_hash followed by
 // engram_gather_reduce.
+//
+// Dedup mode (groups from engram_dedup): one wave per (group, module) takes
+// the group's first token, hashes its window and gathers once, then stores
+// the vector to every member, as gather_reduce_kernel does in dedup mode.
+// Equal windows give equal addresses, so this is bitwise the direct result,
+// with one hash and one gather per distinct window.
 #include "batch_order.h"
 #include "row_sum.h"
 
@@ -36,19 +42,46 @@ __device__ __forceinline__ uint32_t mod_rows(uint64_t x, uint64_t R, uint64_t ma
     return static_cast<uint32_t>(r);
 }
 
-template <bool POW2, int FMT>
-__global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const int32_t* __restrict__ ids,
-                                                     const int32_t* __restrict__ history, uint32_t item_base,
+// Token ids and, in dedup mode, the groups that engram_dedup wrote.
+struct Tokens {
+    const int32_t* ids;
+    const int32_t* history;
+    uint32_t n_tok;
+    const int32_t* perm;      // dedup mode only
+    const int32_t* offsets;
+    const int32_t* n_unique;
+};
+
+template <bool POW2, int FMT, bool kDedup>
+__global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const Tokens T, uint32_t item_base,
                                                      uint32_t item_end, BatchOrder batch, float* __restrict__ out) {
+    const int32_t* __restrict__ ids = T.ids;
+    const int32_t* __restrict__ history = T.history;
     const uint32_t b = blockIdx.x;
     const uint32_t m = b & 1u;  // block b: module b % 2 of 4 consecutive items
     const uint32_t group = b >> 1;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t item = item_base + group * 4u + wave;
-    if (item >= item_end) return;
-    uint32_t seq, t;
-    const uint32_t tok = batched_token(item, batch, &seq, &t);
+
+    uint32_t limit = item_end;
+    if (kDedup) {
+        const int32_t nu = *T.n_unique;  // negative: the dedup call failed, there are no groups
+        limit = nu > 0 ? min(limit, static_cast<uint32_t>(nu)) : 0u;
+    }
+    if (item >= limit) return;
+    uint32_t seq, t, tok;
+    if (kDedup) {
+        // the group's first member; its position in its sequence gives the window
+        const uint32_t first = static_cast<uint32_t>(T.offsets[item]);
+        if (first >= T.n_tok) return;
+        tok = static_cast<uint32_t>(T.perm[first]);
+        if (tok >= T.n_tok) return;
+        seq = tok / batch.seq_len;
+        t = tok - seq * batch.seq_len;
+    } else {
+        tok = batched_token(item, batch, &seq, &t);
+    }
 
     // Window of the token (wave-uniform): w[k] = id k positions back, else history, else 0.
     uint64_t w[ENGRAM_MAX_ORDER];
@@ -72,40 +105,59 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
     RowSet r;
     load_rows<FMT>(P.g, s0, a, lane, r);
     const f32x4 acc = sum_rows<FMT>(r, lane);
-    __builtin_nontemporal_store(
-        acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + m * kRowBytes + lane * 4u));
+    const size_t col = static_cast<size_t>(m) * kRowBytes + lane * 4u;
+    if (!kDedup) {
+        __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + col));
+    } else {
+        // every group has a member (the token above): the first store is
+        // unconditional, as in gather_reduce_kernel's dedup mode
+        uint32_t i = static_cast<uint32_t>(T.offsets[item]);
+        const uint32_t end = min(static_cast<uint32_t>(T.offsets[item + 1]), T.n_tok);
+        do {
+            const uint32_t u = static_cast<uint32_t>(T.perm[i]);
+            if (u < T.n_tok)
+                __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(u) * (2 * kRowBytes) + col));
+        } while (++i < end);
+    }
+}
+
+template <bool POW2, int FMT>
+void launch_one(const LookupParams& p, const Tokens& tk, dim3 grid, uint32_t base, uint32_t end,
+                const BatchOrder& batch, float* out, hipStream_t stream) {
+    if (tk.perm)
+        hipLaunchKernelGGL((lookup_kernel<POW2, FMT, true>), grid, dim3(256), 0, stream, p, tk, base, end, batch, out);
+    else
+        hipLaunchKernelGGL((lookup_kernel<POW2, FMT, false>), grid, dim3(256), 0, stream, p, tk, base, end, batch, out);
 }
 
 }  // namespace
 
 hipError_t launch_lookup(const HashParams& h, const GatherParams& g, const int32_t* ids, const int32_t* history,
-                         uint32_t n_tok, uint32_t seq_len, float* out, hipStream_t stream) {
+                         uint32_t n_tok, uint32_t seq_len, const int32_t* perm, const int32_t* offsets,
+                         const int32_t* n_unique, float* out, hipStream_t stream) {
     LookupParams p;
     p.h = h;
     p.g = g;
+    const Tokens tk{ids, history, n_tok, perm, offsets, n_unique};
     bool pow2 = true;
     for (int s = 0; s < kSub; ++s) pow2 = pow2 && (h.rows[s] & (h.rows[s] - 1u)) == 0;
-    // Launches cover at most 2^24 items so the grid stays far below 2^32
-    // threads.
+    // Launches cover at most 2^24 items (tokens, or groups in dedup mode) so
+    // the grid stays far below 2^32 threads.
     constexpr uint32_t kChunk = 1u << 24;
     const bool mx = g.scale_format == ENGRAM_SCALE_E8M0_BLOCK32;
     const BatchOrder batch = batch_order(n_tok, seq_len);
     for (uint32_t base = 0; base < n_tok; base += kChunk) {
         const uint32_t n = min(kChunk, n_tok - base);
         const uint32_t groups = ((n + 3u) / 4u + 3u) & ~3u;
-        const dim3 grid(2u * groups), block(256);
+        const dim3 grid(2u * groups);
         if (pow2 && mx)
-            hipLaunchKernelGGL((lookup_kernel<true, ENGRAM_SCALE_E8M0_BLOCK32>), grid, block, 0, stream, p, ids, history,
-                               base, base + n, batch, out);
+            launch_one<true, ENGRAM_SCALE_E8M0_BLOCK32>(p, tk, grid, base, base + n, batch, out, stream);
         else if (pow2)
-            hipLaunchKernelGGL((lookup_kernel<true, ENGRAM_SCALE_F32_ROW>), grid, block, 0, stream, p, ids, history, base,
-                               base + n, batch, out);
+            launch_one<true, ENGRAM_SCALE_F32_ROW>(p, tk, grid, base, base + n, batch, out, stream);
         else if (mx)
-            hipLaunchKernelGGL((lookup_kernel<false, ENGRAM_SCALE_E8M0_BLOCK32>), grid, block, 0, stream, p, ids,
-                               history, base, base + n, batch, out);
+            launch_one<false, ENGRAM_SCALE_E8M0_BLOCK32>(p, tk, grid, base, base + n, batch, out, stream);
         else
-            hipLaunchKernelGGL((lookup_kernel<false, ENGRAM_SCALE_F32_ROW>), grid, block, 0, stream, p, ids, history,
-                               base, base + n, batch, out);
+            launch_one<false, ENGRAM_SCALE_F32_ROW>(p, tk, grid, base, base + n, batch, out, stream);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -286,6 +286,30 @@ int engram_lookup(engram_plan_t plan, const int32_t* ids, const int32_t* history
                   int64_t n_seq, int64_t seq_len, float* out, void* stream);
 
 /*
+ * engram_lookup in dedup mode: one hash and one gather per group of tokens
+ * with equal windows, the vector stored to every member of the group.  Equal
+ * windows hash to equal rows [VRAM; GUIDE "Engram"], so the result is bitwise
+ * that of engram_lookup (and of engram_hash + engram_gather_reduce in either
+ * mode); the address buffer and the separate hash launch are gone, and a
+ * window repeated across a batch (a shared prefix [BLOG]) is hashed once.
+ *
+ *   ids, history, n_seq, seq_len   as for engram_lookup, and the same tokens
+ *             that engram_dedup grouped.
+ *   perm, offsets, n_unique        as written by engram_dedup for those
+ *             tokens (device int32, 4-byte aligned); *n_unique stays on the
+ *             device.  *n_unique < 0 (a failed dedup call) writes nothing.
+ *   out       device fp32 [n_seq*seq_len][2][256], 16-byte aligned (output).
+ *
+ * The grid covers n_seq*seq_len groups and exits early past *n_unique.  A
+ * perm or offsets entry out of [0, n_tok) is skipped, never dereferenced.
+ * n_seq*seq_len == 0 is a no-op.  Errors: EINVAL (NULL/misaligned pointer),
+ * ERANGE as engram_hash.
+ */
+int engram_lookup_dedup(engram_plan_t plan, const int32_t* ids, const int32_t* history,
+                        int64_t n_seq, int64_t seq_len, const int32_t* perm, const int32_t* offsets,
+                        const int32_t* n_unique, float* out, void* stream);
+
+/*
  * Workspace bytes engram_dedup needs for n_tok tokens under this plan
  * (host-only).  The size depends on the plan's vocab_size, which bounds the
  * width of the sort keys.  Errors: EINVAL (NULL plan or bytes), ERANGE

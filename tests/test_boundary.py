@@ -252,6 +252,25 @@ def test_lookup_validation(hg, plan):
     assert L.engram_lookup(plan, FAKE, FAKE + 2, 1, 1, FAKE, None) == EINVAL
 
 
+def test_lookup_dedup_validation(hg, plan):
+    L = hg.lib()
+    G = (FAKE + 64, FAKE + 128, FAKE + 192)  # perm, offsets, n_unique
+    assert L.engram_lookup_dedup(None, FAKE, None, 1, 1, *G, FAKE, None) == EINVAL
+    assert L.engram_lookup_dedup(plan, FAKE, None, 0, 5, *G, FAKE, None) == OK
+    assert L.engram_lookup_dedup(plan, FAKE, None, 0, 5, None, None, None, FAKE, None) == OK
+    assert L.engram_lookup_dedup(plan, FAKE, None, -1, 5, *G, FAKE, None) == EINVAL
+    assert L.engram_lookup_dedup(plan, FAKE, None, 1 << 16, 1 << 15, *G, FAKE, None) == ERANGE
+    assert L.engram_lookup_dedup(plan, None, None, 1, 1, *G, FAKE, None) == EINVAL
+    assert L.engram_lookup_dedup(plan, FAKE, None, 1, 1, *G, FAKE + 4, None) == EINVAL
+    assert L.engram_lookup_dedup(plan, FAKE, FAKE + 2, 1, 1, *G, FAKE, None) == EINVAL
+    for k in range(3):  # every group pointer is required and 4-byte aligned
+        missing, skewed = list(G), list(G)
+        missing[k] = None
+        skewed[k] = G[k] + 2
+        assert L.engram_lookup_dedup(plan, FAKE, None, 1, 1, *missing, FAKE, None) == EINVAL
+        assert L.engram_lookup_dedup(plan, FAKE, None, 1, 1, *skewed, FAKE, None) == EINVAL
+
+
 def test_plan_scale_formats(hg):
     M = hg.measure_lib()
     L = hg.lib()
@@ -336,7 +355,8 @@ def test_gather_reduce_batched_validation(hg, plan):
 
 
 def test_binding_rejects_groups_of_another_size(hg):
-    """dedup() and gather_reduce() refuse a Groups sized for another token count before any call is made."""
+    """dedup(), gather_reduce() and lookup() refuse a Groups sized for another token count before any call is
+    made."""
     import torch
     ids = torch.zeros((2, 50), dtype=torch.int32)
     addr = torch.zeros((100, 48), dtype=torch.int32).view(torch.uint32)
@@ -353,6 +373,8 @@ def test_binding_rejects_groups_of_another_size(hg):
             hg.dedup(None, ids, groups=g)
         with pytest.raises(ValueError, match="groups"):
             hg.gather_reduce(None, addr, groups=g)
+        with pytest.raises(ValueError, match="groups"):
+            hg.lookup(None, ids, groups=g)
 
 
 def test_dedup_noalloc_validation(hg, plan):
