@@ -421,11 +421,13 @@ def main(argv=None) -> int:
     flush = torch.ones(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib > 0 else None
     flush_sink = torch.zeros((), dtype=torch.uint8, device=dev)
 
-    def run_steps(n: int, pipelined: bool, ev=None) -> None:
+    def run_steps(n: int, pipelined: bool, ev=None, stages: bool = False) -> None:
         """n steps.  Step i hashes (and groups) batch i into buffer i % 2, then gathers that buffer.  Pipelined, the
         hash and dedup of batch i + 1 run on side streams while batch i is gathered -- they depend on the ids
         alone -- and wait only for the gather that last read their buffer; serial, everything runs in order on one
-        stream.  ev[i] = 6 events around step i's hash, dedup and gather."""
+        stream.  ev[i] = 6 events around step i's hash, dedup and gather; only the gather's pair is recorded unless
+        ``stages`` (each recorded pair adds a few us of queue work to the step)."""
+        stage_ev = ev if stages else None
         freed = [torch.cuda.Event(), torch.cuda.Event()]  # the gather that last read buffer k has finished
 
         def produce(i):
@@ -435,11 +437,11 @@ def main(argv=None) -> int:
                 hs.wait_event(freed[k])
             done = []
             if not fused_dedup:
-                if ev:
-                    ev[i][0].record(hs)
+                if stage_ev:
+                    stage_ev[i][0].record(hs)
                 hg.hash(plan, b[1], b[2], out=addr_bufs[k], stream=hs)
-                if ev:
-                    ev[i][1].record(hs)
+                if stage_ev:
+                    stage_ev[i][1].record(hs)
                 if pipelined:
                     done.append(torch.cuda.Event())
                     done[-1].record(hs)
@@ -447,11 +449,11 @@ def main(argv=None) -> int:
                 ds = s_dedup if pipelined else stream
                 if pipelined:
                     ds.wait_event(freed[k])
-                if ev:
-                    ev[i][2].record(ds)
+                if stage_ev:
+                    stage_ev[i][2].record(ds)
                 hg.dedup(plan, b[1], b[2], workspace=ws, groups=group_bufs[k], stream=ds)
-                if ev:
-                    ev[i][3].record(ds)
+                if stage_ev:
+                    stage_ev[i][3].record(ds)
                 if pipelined:
                     done.append(torch.cuda.Event())
                     done[-1].record(ds)
@@ -493,6 +495,15 @@ def main(argv=None) -> int:
     run_steps(args.steps, pipelined, ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # per-stage times (hash, dedup, gather) from a separate, shorter run with an event pair around every stage
+    n_stage = min(args.steps, 200)
+    ev_stage = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_stage)]
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    run_steps(n_stage, pipelined, ev_stage, stages=True)
+    torch.cuda.synchronize()
+    stage_us = (time.perf_counter() - t2) / n_stage * 1e6
 
     serial = None
     if pipelined:
@@ -596,8 +607,8 @@ def main(argv=None) -> int:
     keys |= np.arange(48, dtype=np.uint64)[None, :] << np.uint64(32)
     distinct = int(np.unique(keys).size)
 
-    hash_ms = None if fused_dedup else float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    dedup_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) if args.dedup else None
+    hash_ms = None if fused_dedup else float(np.mean([e[0].elapsed_time(e[1]) for e in ev_stage]))
+    dedup_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev_stage])) if args.dedup else None
     gather_ms = float(np.mean([e[4].elapsed_time(e[5]) for e in ev]))
     ms_per_step = wall / args.steps * 1e3
     tok_s = n_tok / (ms_per_step / 1e3)
@@ -679,6 +690,10 @@ def main(argv=None) -> int:
         "gather_ms": gather_ms,
         "hash_ms": hash_ms,
         "dedup_ms": dedup_ms,
+        "stage_timing": {"steps": n_stage, "us_per_step": stage_us,
+                         "gather_ms": float(np.mean([e[4].elapsed_time(e[5]) for e in ev_stage])),
+                         "note": "hash_ms and dedup_ms come from this separate run, with an event pair around every "
+                                 "stage; the timed steps record only the gather's pair"},
         "us_per_step": ms_per_step * 1e3,
         "hash_gbps": None if hash_ms is None else HASH_BYTES_PER_TOKEN * n_tok / (hash_ms / 1e3) / 1e9,
         "gather_bytes_per_launch": gather_bytes,

@@ -32,18 +32,18 @@
 // A stale or uninitialised entry that happens to equal the stamp only adds a
 // rank nobody uses: ranks stay strictly increasing over the ids in use.
 //
-// One kernel per pass (onesweep): a tile of 8,192 elements ranks its
-// elements by digit (wave ballots, stable), publishes its per-digit counts,
-// and finds the counts of all earlier tiles by decoupled look-back: each
-// tile's status word per digit holds its count (state AGG) and, once known,
-// its inclusive prefix (state INC).  A wave reads the statuses of 64 earlier
-// tiles of one digit in one coalesced load (statuses are stored digit-major)
-// and sums back to the nearest INC, so a tile needs about T / 64 dependent
-// loads per digit, not T.  Tiles take their index from an atomic counter in
-// start order, so every tile waited on has started and publishes without
-// waiting on anyone: the waits end.  They are also bounded: past a spin
-// limit the tile records an error and stops waiting, every later wait and
-// pass gives up, and the group count comes out as -1.
+// One kernel per pass: a tile of 4,096 elements ranks its elements by digit
+// (wave ballots, stable), publishes its 256 digit counts (two 16-bit counts
+// per status word, each with a ready bit), and sums the published counts of
+// all earlier tiles, which with the pass's digit totals gives where each of
+// its digits starts in the output.  The tile then scatters its elements.
+// Tiles take their index from an atomic counter in start order, so every
+// tile waited on has started and publishes before it waits on anyone: the
+// waits end.  They are also bounded: past a spin limit a wait records an
+// error and gives up, any other wait still pending gives up too, a tile
+// whose wait gave up writes nothing, and the group count comes out as -1.
+// Positions are checked against n before every store, so no outcome writes
+// out of bounds.
 //
 // Kernels of one call, in stream order:
 //   init    clear counters, histograms and statuses; mark the ids in use
@@ -104,6 +104,8 @@ struct Ctl {
     uint32_t pad1[46];
 };
 static_assert(sizeof(Ctl) == 512, "control block size");
+// The group kernel's look-back reads one earlier tile per thread.
+static_assert((kMaxDedupTokens + kTile - 1) / kTile <= kPassThreads, "tiles per call");
 
 struct Ids {
     const int32_t* ids;
@@ -297,12 +299,14 @@ __global__ __launch_bounds__(256) void bitmap_kernel(uint32_t vocab, Workspace w
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t stamp = w.ctl->stamp + 1u;
     const uint32_t word0 = blockIdx.x * 64u + wave * 16u;  // this wave's 16 words
+    // all 16 loads issued before the first is used (ids past the vocabulary
+    // read its last entry and are masked below), so the wave waits once
+    uint32_t f[16];
+#pragma unroll
+    for (uint32_t c = 0; c < 16; ++c) f[c] = w.flags[min(((word0 + c) << 6) + lane, vocab - 1u)];
     uint64_t word[16];
 #pragma unroll
-    for (uint32_t c = 0; c < 16; ++c) {
-        const uint32_t id = ((word0 + c) << 6) + lane;
-        word[c] = __ballot(id < vocab && w.flags[id] == stamp);
-    }
+    for (uint32_t c = 0; c < 16; ++c) word[c] = __ballot(((word0 + c) << 6) + lane < vocab && f[c] == stamp);
     uint64_t mine = 0;
 #pragma unroll
     for (uint32_t c = 0; c < 16; ++c)
@@ -321,13 +325,14 @@ __global__ __launch_bounds__(256) void bitmap_kernel(uint32_t vocab, Workspace w
 }
 
 // ---------------------------------------------------------------------------
-// keys: pack every window; digit histograms of the passes this call needs.
-// A block stages its 4,096 ids (and the 3 before them) and, with compaction,
-// the whole presence bitmap with its prefix counts in LDS, so a key costs no
-// dependent global loads: rank(id) = ids in use in earlier 4,096-id blocks +
-// ids in use earlier in the block's words + set bits below id in its word.
-// With compaction the first block also records B, the pass count and the
-// stamp for the rest of the call.
+// keys: pack every window; the histogram of the first pass's digit.
+// A block loads its 4,096 ids (and the 3 before them) and, with compaction,
+// stages the whole presence bitmap with its prefix counts in LDS; it ranks
+// each id once into LDS, so a key costs no dependent global loads:
+// rank(id) = ids in use in earlier 4,096-id blocks + ids in use earlier in
+// the block's words + set bits below id in its word.  With compaction the
+// first block also records B, the pass count and the stamp for the rest of
+// the call.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kKeyThreads) void keys_kernel(Ids s, uint32_t n, uint32_t vocab, uint32_t compact,
                                                            Workspace w) {
@@ -335,7 +340,7 @@ __global__ __launch_bounds__(kKeyThreads) void keys_kernel(Ids s, uint32_t n, ui
     constexpr uint32_t kStage = (kKeyTile + 3u + kKeyThreads - 1u) / kKeyThreads;  // staged ids per thread
     constexpr uint32_t kWordsPerThread = 64u * kMaxBitmapBlocks / kKeyThreads;
     constexpr uint32_t kKeyWaves = kKeyThreads / 64;
-    __shared__ int32_t ids_s[kKeyTile + 3];
+    __shared__ uint32_t rank_s[kKeyTile + 3];  // m of the block's ids and the 3 before them
     __shared__ uint64_t bits_s[64 * kMaxBitmapBlocks];
     __shared__ uint32_t wpre_s[64 * kMaxBitmapBlocks];
     __shared__ uint32_t bpre_s[kMaxBitmapBlocks];
@@ -343,34 +348,31 @@ __global__ __launch_bounds__(kKeyThreads) void keys_kernel(Ids s, uint32_t n, ui
     __shared__ uint32_t s_d;
     const uint32_t wave = threadIdx.x >> 6;
     const uint32_t begin = blockIdx.x * kKeyTile;
-    {  // the block's ids and the 3 before them; every load issued before the first store
-        int32_t v[kStage];
+    // Every global load of the staging -- the block's ids and the 3 before
+    // them, and with compaction the bitmap, its word prefixes and the block
+    // counts -- is issued before the first LDS store, so the block waits for
+    // memory once.
+    const uint32_t blocks = compact ? (vocab + kRankIds - 1u) / kRankIds : 0u;
+    const uint32_t words = 64u * blocks;
+    int32_t v[kStage];
 #pragma unroll
-        for (uint32_t c = 0; c < kStage; ++c) {
-            const uint32_t i = c * kKeyThreads + threadIdx.x;
-            const int64_t tok = int64_t(begin) + int64_t(i) - 3;
-            v[c] = (i < kKeyTile + 3u && tok >= 0 && tok < int64_t(n)) ? s.ids[tok] : 0;
-        }
-#pragma unroll
-        for (uint32_t c = 0; c < kStage; ++c) {
-            const uint32_t i = c * kKeyThreads + threadIdx.x;
-            if (i < kKeyTile + 3u) ids_s[i] = v[c];
-        }
+    for (uint32_t c = 0; c < kStage; ++c) {
+        const uint32_t i = c * kKeyThreads + threadIdx.x;
+        const int64_t tok = int64_t(begin) + int64_t(i) - 3;
+        v[c] = (i < kKeyTile + 3u && tok >= 0 && tok < int64_t(n)) ? s.ids[tok] : 0;
     }
+    uint64_t bw[kWordsPerThread];
+    uint32_t pw[kWordsPerThread];
+#pragma unroll
+    for (uint32_t c = 0; c < kWordsPerThread; ++c) {
+        const uint32_t i = c * kKeyThreads + threadIdx.x;
+        bw[c] = i < words ? w.bitmap[i] : 0u;
+        pw[c] = i < words ? w.wpre[i] : 0u;
+    }
+    const uint32_t bc = threadIdx.x < blocks ? w.bcount[threadIdx.x] : 0u;
     for (uint32_t i = threadIdx.x; i < kKeyWaves * kRadix; i += kKeyThreads) (&h[0][0])[i] = 0u;
     uint32_t b, has_hi, n_ids = 0;
     if (compact) {
-        const uint32_t blocks = (vocab + kRankIds - 1u) / kRankIds;
-        const uint32_t words = 64u * blocks;
-        uint64_t bw[kWordsPerThread];
-        uint32_t pw[kWordsPerThread];
-#pragma unroll
-        for (uint32_t c = 0; c < kWordsPerThread; ++c) {
-            const uint32_t i = c * kKeyThreads + threadIdx.x;
-            bw[c] = i < words ? w.bitmap[i] : 0u;
-            pw[c] = i < words ? w.wpre[i] : 0u;
-        }
-        const uint32_t bc = threadIdx.x < blocks ? w.bcount[threadIdx.x] : 0u;
 #pragma unroll
         for (uint32_t c = 0; c < kWordsPerThread; ++c) {
             const uint32_t i = c * kKeyThreads + threadIdx.x;
@@ -406,7 +408,27 @@ __global__ __launch_bounds__(kKeyThreads) void keys_kernel(Ids s, uint32_t n, ui
         has_hi = w.ctl->has_hi;
         __syncthreads();
     }
+    // m of an id: its rank among the ids in use (compaction), else its low B bits
     const uint32_t mask = (1u << b) - 1u;
+    auto rank_of = [&](uint32_t id) -> uint32_t {
+        if (!compact) return id & mask;
+        if (id >= vocab) return n_ids;  // ids out of range share the rank after the last
+        const uint32_t wd = id >> 6;
+        return bpre_s[id >> 12] + wpre_s[wd] +
+               static_cast<uint32_t>(__popcll(bits_s[wd] & ((uint64_t(1) << (id & 63u)) - 1u)));
+    };
+    // Each staged id is ranked once (a window reads each of its ids' ranks
+    // from LDS; ranking per window would look every id up four times).
+#pragma unroll
+    for (uint32_t c = 0; c < kStage; ++c) {
+        const uint32_t i = c * kKeyThreads + threadIdx.x;
+        if (i < kKeyTile + 3u) rank_s[i] = rank_of(static_cast<uint32_t>(v[c]));
+    }
+    __syncthreads();
+    // All keys of the thread first, then their stores: a store between two
+    // keys would make every later wait for memory (a history id) wait for it.
+    uint64_t klo[kKeyItems], khi[kKeyItems];
+#pragma unroll
     for (uint32_t j = 0; j < kKeyItems; ++j) {
         const uint32_t tok = begin + j * kKeyThreads + threadIdx.x;
         const bool valid = tok < n;
@@ -416,30 +438,27 @@ __global__ __launch_bounds__(kKeyThreads) void keys_kernel(Ids s, uint32_t n, ui
             const int32_t t = static_cast<int32_t>(tok - seq * s.seq_len);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {  // w_0 most significant
-                uint32_t id;
-                if (t - k >= 0)
-                    id = static_cast<uint32_t>(ids_s[tok - begin + 3u - static_cast<uint32_t>(k)]);
-                else
-                    id = s.history ? static_cast<uint32_t>(s.history[seq * 3u + static_cast<uint32_t>(3 + t - k)]) : 0u;
                 uint32_t m;
-                if (compact) {
-                    m = n_ids;  // ids out of range share the rank after the last
-                    if (id < vocab) {
-                        const uint32_t wd = id >> 6;
-                        m = bpre_s[id >> 12] + wpre_s[wd] +
-                            static_cast<uint32_t>(__popcll(bits_s[wd] & ((uint64_t(1) << (id & 63u)) - 1u)));
-                    }
-                } else {
-                    m = id & mask;
-                }
+                if (t - k >= 0)
+                    m = rank_s[tok - begin + 3u - static_cast<uint32_t>(k)];
+                else
+                    m = rank_of(s.history ? static_cast<uint32_t>(s.history[seq * 3u + static_cast<uint32_t>(3 + t - k)]) : 0u);
                 hi = (hi << b) | (lo >> (64u - b));
                 lo = (lo << b) | m;
             }
-            w.lo[0][tok] = lo;
-            if (has_hi) w.hi[0][tok] = hi;
+            // histogram of the first pass's digit (each later pass counts its successor's)
+            atomicAdd(&h[wave][static_cast<uint32_t>(lo) & 0xFFu], 1u);
         }
-        // histogram of the first pass's digit (each later pass counts its successor's)
-        if (valid) atomicAdd(&h[wave][static_cast<uint32_t>(lo) & 0xFFu], 1u);
+        klo[j] = lo;
+        khi[j] = hi;
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < kKeyItems; ++j) {
+        const uint32_t tok = begin + j * kKeyThreads + threadIdx.x;
+        if (tok < n) {
+            w.lo[0][tok] = klo[j];
+            if (has_hi) w.hi[0][tok] = khi[j];
+        }
     }
     __syncthreads();
     if (threadIdx.x < kRadix) {
@@ -456,13 +475,7 @@ __global__ __launch_bounds__(kKeyThreads) void keys_kernel(Ids s, uint32_t n, ui
 __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass, uint32_t tiles, Workspace w,
                                                             int32_t* __restrict__ perm) {
     Ctl* ctl = w.ctl;
-    const uint32_t npass = ctl->npass;
-    if (static_cast<uint32_t>(pass) >= npass) return;  // this call's keys need fewer passes
-    const bool has_hi = ctl->has_hi != 0u;
-    const bool last = static_cast<uint32_t>(pass) + 1u == npass;
-    const uint32_t limit = ctl->spin_limit;
-
-    __shared__ uint32_t s_tile;
+    __shared__ uint32_t s_tile, s_failed;
     __shared__ uint32_t wave_hist[kPassWaves][kRadix];  // counts per wave, then exclusive prefixes across waves
     __shared__ uint32_t next_hist[kPassWaves][kRadix];  // this tile's counts of the next pass's digit, per wave
     __shared__ uint32_t tile_cnt[kRadix];
@@ -472,14 +485,28 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
     const uint64_t lt = (uint64_t(1) << lane) - 1u;
+    // The digit totals, the pass count and the ticket are read together (the
+    // loads are issued before the atomic, whose result is waited for first);
+    // a pass the call does not need returns after them (its ticket counter
+    // is reset by the next call).
     uint32_t total = 0;  // this pass's total count of digit threadIdx.x (threads 0..255)
     if (threadIdx.x < kRadix) total = w.hist[pass * kRadix + threadIdx.x];
-    if (threadIdx.x == 0) s_tile = atomicAdd(&ctl->tile_ctr[pass], 1u);
+    const uint32_t npass = ctl->npass;
+    const bool has_hi = ctl->has_hi != 0u;
+    const uint32_t limit = ctl->spin_limit;
+    uint32_t ticket = 0;
+    if (threadIdx.x == 0) ticket = atomicAdd(&ctl->tile_ctr[pass], 1u);
     for (uint32_t i = threadIdx.x; i < kPassWaves * kRadix; i += kPassThreads) {
         (&wave_hist[0][0])[i] = 0u;
         (&next_hist[0][0])[i] = 0u;
     }
+    if (threadIdx.x == 0) {
+        s_tile = ticket;
+        s_failed = 0u;
+    }
     __syncthreads();
+    if (static_cast<uint32_t>(pass) >= npass) return;  // this call's keys need fewer passes
+    const bool last = static_cast<uint32_t>(pass) + 1u == npass;
     const uint32_t tile = s_tile;
     const int src = pass & 1, dst = src ^ 1;
     const uint64_t* __restrict__ lo_in = w.lo[src];
@@ -544,13 +571,14 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
     {  // counts in the earlier tiles: thread (g, i) sums word i of tiles g, g + 8, g + 16, ... below this one
         const uint32_t g = threadIdx.x / kStatusWords, i = threadIdx.x % kStatusWords;
         uint32_t sum_lo = 0, sum_hi = 0;
+        int failed = 0;  // a wait of this thread gave up
         bool counted = last;  // this thread's items are in the next digit's counts (none needed after the last pass)
         for (uint32_t t0 = g; t0 < tile; t0 += 8u * kGroupsOfRows) {
-            uint32_t v[8];
+            uint32_t word[8];
 #pragma unroll
             for (uint32_t j = 0; j < 8; ++j) {
                 const uint32_t t = t0 + j * kGroupsOfRows;
-                v[j] = t < tile ? load_status(counts + size_t(t) * kStatusWords + i) : kPairReady;
+                word[j] = t < tile ? load_status(counts + size_t(t) * kStatusWords + i) : kPairReady;
             }
             if (!counted) {  // while the first loads are in flight: this tile's counts of the next digit
 #pragma unroll
@@ -562,7 +590,8 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
             for (uint32_t j = 0; j < 8; ++j) {
                 const uint32_t t = t0 + j * kGroupsOfRows;
                 if (t < tile) {
-                    const uint32_t c = wait_ready(counts + size_t(t) * kStatusWords + i, v[j], kPairReady, &ctl->error, limit);
+                    const uint32_t c = wait_ready(counts + size_t(t) * kStatusWords + i, word[j], kPairReady, &ctl->error, limit);
+                    failed |= c == 0u;
                     sum_lo += c & 0x7FFFu;
                     sum_hi += (c >> 16) & 0x7FFFu;
                 }
@@ -575,6 +604,7 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
         }
         part[0][g][i] = sum_lo;
         part[1][g][i] = sum_hi;
+        if (failed) s_failed = 1u;
     }
     __syncthreads();
     if (threadIdx.x < kRadix) {
@@ -591,7 +621,10 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
         }
     }
     __syncthreads();
-    if (load_status(&ctl->error) != 0u) return;  // a wait gave up somewhere: the positions are not to be trusted
+    // A wait of this tile gave up: its positions are unknown, so it writes
+    // nothing.  (The error flag it set makes the call report n_unique = -1.
+    // Other tiles still scatter to positions below n.)
+    if (s_failed) return;
 
 #pragma unroll
     for (uint32_t j = 0; j < kItems; ++j) {
@@ -615,62 +648,86 @@ __global__ __launch_bounds__(kPassThreads) void groups_kernel(uint32_t n, uint32
                                                               Workspace w, int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ n_unique) {
     Ctl* ctl = w.ctl;
-    if (load_status(&ctl->error) != 0u) {  // the sort gave up: report it instead of groups
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-            offsets[0] = 0;
-            *n_unique = -1;
-        }
-        return;
-    }
-    __shared__ uint32_t s_tile, s_total, s_excl;
+    __shared__ uint32_t s_tile, s_failed;
     __shared__ uint32_t wcount[kPassWaves];
+    __shared__ uint32_t wexcl[kPassWaves];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
     const uint64_t lt = (uint64_t(1) << lane) - 1u;
-    if (threadIdx.x == 0) s_tile = atomicAdd(&ctl->tile_ctr[kMaxPasses], 1u);
-    __syncthreads();
-    const uint32_t tile = s_tile;
+    // the control words are read before the ticket is taken, so both reads overlap
     const uint32_t q = ctl->npass & 1u;  // buffer the last pass wrote
     const uint32_t limit = ctl->spin_limit;
     const bool has_hi = ctl->has_hi != 0u;
+    uint32_t ticket = 0;
+    if (threadIdx.x == 0) ticket = atomicAdd(&ctl->tile_ctr[kMaxPasses], 1u);
+    if (threadIdx.x == 0) {
+        s_tile = ticket;
+        s_failed = 0u;
+    }
+    __syncthreads();
+    const uint32_t tile = s_tile;
     const uint64_t* __restrict__ lo = w.lo[q];
     const uint64_t* __restrict__ hi = w.hi[q];
     uint32_t* st = w.status + size_t(max_passes) * kStatusWords * tiles;  // [tiles] group counts
 
     const uint32_t first = tile * kTile + wave * kWaveSpan;
+    // Every key and its predecessor are loaded before the first comparison
+    // (indices clamped to [0, n); n >= 1 here), so the wave waits once.
+    // Without high key words the high loads read the low words again (cache
+    // hits) and their comparison is masked: no load sits behind a branch.
+    const uint64_t* __restrict__ hsrc = has_hi ? hi : lo;
+    uint64_t cur[kItems], prev[kItems], cur_hi[kItems], prev_hi[kItems];
+#pragma unroll
+    for (uint32_t j = 0; j < kItems; ++j) {
+        const uint32_t i = min(first + j * 64u + lane, n - 1u);
+        const uint32_t ip = i == 0 ? 0u : i - 1u;
+        cur[j] = lo[i];
+        prev[j] = lo[ip];
+        cur_hi[j] = hsrc[i];
+        prev_hi[j] = hsrc[ip];
+    }
     uint64_t m[kItems];
     uint32_t cnt = 0;
 #pragma unroll
     for (uint32_t j = 0; j < kItems; ++j) {
         const uint32_t i = first + j * 64u + lane;
-        bool f = false;
-        if (i < n) f = i == 0 || lo[i] != lo[i - 1] || (has_hi && hi[i] != hi[i - 1]);
+        const bool f = i < n && (i == 0 || cur[j] != prev[j] || (has_hi && cur_hi[j] != prev_hi[j]));
         m[j] = __ballot(f);
         cnt += static_cast<uint32_t>(__popcll(m[j]));
     }
     if (lane == 0) wcount[wave] = cnt;
     __syncthreads();
-    if (wave == 0) {
+    if (threadIdx.x == 0) {
         uint32_t total = 0;
         for (uint32_t k = 0; k < kPassWaves; ++k) total += wcount[k];
-        if (lane == 0) store_status(st + tile, kWordReady | total);
-        uint32_t acc = 0;  // groups in the earlier tiles, lane by lane
-        for (uint32_t t0 = 0; t0 < tile; t0 += 64u) {
-            const uint32_t t = t0 + lane;
-            if (t < tile) acc += wait_ready(st + t, load_status(st + t), kWordReady, &ctl->error, limit) & ~kWordReady;
+        store_status(st + tile, kWordReady | total);
+    }
+    {  // groups in the earlier tiles: wave k sums tiles 64k .. 64k + 63 below this one, all waves at once
+        const uint32_t t = wave * 64u + lane;
+        uint32_t c = 0;
+        if (t < tile) {
+            c = wait_ready(st + t, load_status(st + t), kWordReady, &ctl->error, limit);
+            if (c == 0u) s_failed = 1u;
         }
-        const uint32_t excl = wave_sum(acc);
-        if (lane == 0) {
-            s_total = total;
-            s_excl = excl;
-        }
+        const uint32_t sum = wave_sum(c & ~kWordReady);
+        if (lane == 0) wexcl[wave] = sum;
     }
     __syncthreads();
-    if (load_status(&ctl->error) != 0u) {  // a wait gave up: report it instead of a count
-        if (threadIdx.x == 0) *n_unique = -1;
+    // A wait of this tile gave up: its positions are unknown, so it writes no
+    // offsets.  The tile that writes n_unique also reports a wait that gave
+    // up anywhere in the call, in the sort or here, as -1.
+    const bool last_tile = tile == tiles - 1u;
+    if (s_failed || (last_tile && load_status(&ctl->error) != 0u)) {
+        if (last_tile && threadIdx.x == 0) *n_unique = -1;
         return;
     }
-    uint32_t pos = s_excl;
+    uint32_t excl = 0, total = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kPassWaves; ++k) {
+        excl += wexcl[k];
+        total += wcount[k];
+    }
+    uint32_t pos = excl;
     for (uint32_t k = 0; k < wave; ++k) pos += wcount[k];
 #pragma unroll
     for (uint32_t j = 0; j < kItems; ++j) {
@@ -680,8 +737,8 @@ __global__ __launch_bounds__(kPassThreads) void groups_kernel(uint32_t n, uint32
         }
         pos += static_cast<uint32_t>(__popcll(m[j]));
     }
-    if (tile == tiles - 1u && threadIdx.x == 0) {
-        const uint32_t total = s_excl + s_total;
+    if (last_tile && threadIdx.x == 0) {
+        total += excl;
         if (total <= n) offsets[total] = static_cast<int32_t>(n);
         *n_unique = static_cast<int32_t>(total);
     }
