@@ -87,6 +87,7 @@ constexpr uint32_t kPairReady = 0x80008000u;
 constexpr uint32_t kWordReady = 0x80000000u;
 constexpr uint32_t kStatusWords = kRadix / 2;  // words per pass tile
 constexpr uint32_t kGroupsOfRows = kPassThreads / kStatusWords;  // earlier tiles read in parallel per thread column
+constexpr uint32_t kLookAhead = 16;  // status loads in flight per thread in a pass's look-back
 
 // Control block at the start of the workspace.
 struct Ctl {
@@ -568,15 +569,16 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
         for (uint32_t k = 0; k < wave; ++k) pre += wsum[k];
         base[threadIdx.x] += pre;
     }
-    {  // counts in the earlier tiles: thread (g, i) sums word i of tiles g, g + 8, g + 16, ... below this one
+    {  // counts in the earlier tiles: thread (g, i) sums word i of tiles g, g + 8, g + 16, ... below this one,
+       // kLookAhead loads in flight (one round for up to 8 x kLookAhead earlier tiles)
         const uint32_t g = threadIdx.x / kStatusWords, i = threadIdx.x % kStatusWords;
         uint32_t sum_lo = 0, sum_hi = 0;
         int failed = 0;  // a wait of this thread gave up
         bool counted = last;  // this thread's items are in the next digit's counts (none needed after the last pass)
-        for (uint32_t t0 = g; t0 < tile; t0 += 8u * kGroupsOfRows) {
-            uint32_t word[8];
+        for (uint32_t t0 = g; t0 < tile; t0 += kLookAhead * kGroupsOfRows) {
+            uint32_t word[kLookAhead];
 #pragma unroll
-            for (uint32_t j = 0; j < 8; ++j) {
+            for (uint32_t j = 0; j < kLookAhead; ++j) {
                 const uint32_t t = t0 + j * kGroupsOfRows;
                 word[j] = t < tile ? load_status(counts + size_t(t) * kStatusWords + i) : kPairReady;
             }
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
                 counted = true;
             }
 #pragma unroll
-            for (uint32_t j = 0; j < 8; ++j) {
+            for (uint32_t j = 0; j < kLookAhead; ++j) {
                 const uint32_t t = t0 + j * kGroupsOfRows;
                 if (t < tile) {
                     const uint32_t c = wait_ready(counts + size_t(t) * kStatusWords + i, word[j], kPairReady, &ctl->error, limit);

@@ -216,7 +216,7 @@ def test_dedup_vocab_bounds_of_compaction(vocab):
 
 def test_dedup_at_the_token_limit():
     """2^22 tokens, the most one call takes (1,024 tiles: every pass tile sums up to 1,023 earlier tiles' counts in
-    16 rounds of loads per thread column), ids uniform over a 129,280-id vocabulary (17-bit compacted keys)."""
+    8 rounds of 16 loads per thread column), ids uniform over a 129,280-id vocabulary (17-bit compacted keys)."""
     n_seq, seq_len = 4, 1 << 20
     _say(f"dedup {n_seq} x {seq_len} tokens (the per-call limit)")
     rng = np.random.default_rng(22)
