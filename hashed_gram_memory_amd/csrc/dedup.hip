@@ -114,15 +114,6 @@ struct Ids {
     uint32_t seq_len;
 };
 
-// w_k of token tok: the id k positions back, else history, else 0.
-__device__ __forceinline__ uint32_t window_word(const Ids& s, uint32_t tok, int k) {
-    const uint32_t seq = tok / s.seq_len;
-    const int32_t t = static_cast<int32_t>(tok - seq * s.seq_len);
-    if (t - k >= 0) return static_cast<uint32_t>(s.ids[tok - k]);
-    if (s.history) return static_cast<uint32_t>(s.history[seq * 3u + static_cast<uint32_t>(3 + t - k)]);
-    return 0u;
-}
-
 __device__ __forceinline__ uint32_t load_status(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
