@@ -109,6 +109,48 @@ int main(int argc, char** argv) {
         return 1;
     }
 
+    /* dedup: ids with period 5, so most windows repeat; the tokens are grouped, then looked up once per group
+       (engram_lookup_dedup) and once per group from the addresses (engram_gather_reduce in dedup mode): both must
+       be the direct lookup's result, bit for bit */
+    int32_t* h_rep = (int32_t*)malloc(n_tok * sizeof(int32_t));
+    for (int64_t i = 0; i < n_tok; ++i) h_rep[i] = (int32_t)(i % 5);
+    int32_t *rep, *perm, *offsets, *n_unique;
+    uint32_t* rep_addr;
+    float *rep_direct, *rep_dedup, *rep_gather;
+    size_t ws_bytes = 0;
+    void* ws;
+    CHECK_ENGRAM(engram_dedup_workspace(plan, n_tok, &ws_bytes));
+    CHECK_HIP(hipMalloc((void**)&rep, n_tok * sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&perm, n_tok * sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&offsets, (n_tok + 1) * sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&n_unique, sizeof(int32_t)));
+    CHECK_HIP(hipMalloc((void**)&rep_addr, n_tok * ENGRAM_N_SUB * sizeof(uint32_t)));
+    CHECK_HIP(hipMalloc((void**)&rep_direct, out_bytes));
+    CHECK_HIP(hipMalloc((void**)&rep_dedup, out_bytes));
+    CHECK_HIP(hipMalloc((void**)&rep_gather, out_bytes));
+    CHECK_HIP(hipMalloc(&ws, ws_bytes));
+    CHECK_HIP(hipMemcpyAsync(rep, h_rep, n_tok * sizeof(int32_t), hipMemcpyHostToDevice, stream));
+    CHECK_ENGRAM(engram_dedup(plan, rep, NULL, 1, n_tok, perm, offsets, n_unique, ws, ws_bytes, stream));
+    CHECK_ENGRAM(engram_lookup(plan, rep, NULL, 1, n_tok, rep_direct, stream));
+    CHECK_ENGRAM(engram_lookup_dedup(plan, rep, NULL, 1, n_tok, perm, offsets, n_unique, rep_dedup, stream));
+    CHECK_ENGRAM(engram_hash(plan, rep, NULL, 1, n_tok, rep_addr, stream));
+    CHECK_ENGRAM(engram_gather_reduce(plan, rep_addr, n_tok, perm, offsets, n_unique, rep_gather, stream));
+    float* h_rep_direct = (float*)malloc(out_bytes);
+    float* h_rep_dedup = (float*)malloc(out_bytes);
+    float* h_rep_gather = (float*)malloc(out_bytes);
+    int32_t h_n_unique = -2;
+    CHECK_HIP(hipMemcpyAsync(h_rep_direct, rep_direct, out_bytes, hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipMemcpyAsync(h_rep_dedup, rep_dedup, out_bytes, hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipMemcpyAsync(h_rep_gather, rep_gather, out_bytes, hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipMemcpyAsync(&h_n_unique, n_unique, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    if (h_n_unique <= 0 || memcmp(h_rep_dedup, h_rep_direct, out_bytes) != 0 ||
+        memcmp(h_rep_gather, h_rep_direct, out_bytes) != 0) {
+        fprintf(stderr, "dedup-mode lookup or gather differs from the direct lookup (n_unique %d)\n", h_n_unique);
+        return 1;
+    }
+    printf("dedup groups: %d\n", h_n_unique);
+
     FILE* f = fopen(argv[1], "wb");
     if (!f) return 1;
     fwrite(h_ids, sizeof(int32_t), n_tok, f);
@@ -131,6 +173,19 @@ int main(int argc, char** argv) {
     free(h_out);
     free(h_fused);
     free(h_batched);
+    CHECK_HIP(hipFree(rep));
+    CHECK_HIP(hipFree(perm));
+    CHECK_HIP(hipFree(offsets));
+    CHECK_HIP(hipFree(n_unique));
+    CHECK_HIP(hipFree(rep_addr));
+    CHECK_HIP(hipFree(rep_direct));
+    CHECK_HIP(hipFree(rep_dedup));
+    CHECK_HIP(hipFree(rep_gather));
+    CHECK_HIP(hipFree(ws));
+    free(h_rep);
+    free(h_rep_direct);
+    free(h_rep_dedup);
+    free(h_rep_gather);
     printf("c_abi_demo ok: %lld tokens\n", (long long)n_tok);
     return 0;
 }

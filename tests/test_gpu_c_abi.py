@@ -1,4 +1,5 @@
-"""The C ABI from a plain C program (no Python, no torch in its process), checked against the oracle."""
+"""The C ABI from a plain C program (no Python, no torch in its process), checked against the oracle: hash,
+gather, fused lookup, the batch-order gather, and dedup with both dedup-mode calls."""
 import os
 import subprocess
 
@@ -35,3 +36,7 @@ def test_c_program_matches_oracle(tmp_path):
     assert np.array_equal(addr, want_addr)
     assert_within_tolerance(out, want, abs_sum)
     assert np.array_equal(fused, out)
+    # the program's dedup case (ids i mod 5; dedup-mode results compared bitwise with the direct lookup inside it)
+    groups = [int(line.split(":")[1]) for line in r.stdout.splitlines() if line.startswith("dedup groups:")]
+    rep = (np.arange(n_tok) % 5).astype(np.int32).reshape(1, n_tok)
+    assert groups == [oracle.dedup(oracle.windows(rep))[2]]
