@@ -575,7 +575,8 @@ def main(argv=None) -> int:
                  "bytes_per_launch": fused_bytes, "frac": fused_bytes / (t_fused / 1e3) / 1e9 / HBM_PEAK_GBPS}
 
     # the gate-input calls on the first batch's addresses (one batch replayed): per-module sums with one
-    # weight per row, and the 48 dequantised rows un-reduced (fp32 [n_tok, 48, 256], 48 KiB per token)
+    # weight per row, and the 48 dequantised rows un-reduced (fp32 [n_tok, 48, 256], 48 KiB per token); and the
+    # opt-in input check over the same ids and addresses
     scale_bytes = 48 * (8 if mx else 4)  # per token
     gate = None
     if not args.dedup and n_tok <= 131072:
@@ -590,8 +591,16 @@ def main(argv=None) -> int:
         del rows_out, weights
         w_bytes = n_tok * (48 * 256 + scale_bytes + 48 * 4 + 48 * 4 + 2 * 256 * 4)
         r_bytes = n_tok * (48 * 256 + scale_bytes + 48 * 4 + 48 * 256 * 4)
+        # the opt-in range check over the same batch's ids and addresses (engram_check_inputs)
+        counts = torch.empty(3, dtype=torch.int32, device=dev)
+        t_c = _median_ms(torch, lambda: hg.check_inputs(plan, b0[1], b0[2], addr=addr, counts=counts, stream=stream),
+                         stream, 10)
+        c_bytes = n_tok * (4 + 48 * 4) + (0 if b0[2] is None else b0[2].numel() * 4)
         gate = {
             "ids": "first batch, replayed",
+            "check_inputs_us": t_c * 1e3,
+            "check_inputs_bytes_per_launch": c_bytes,
+            "check_inputs_frac": c_bytes / (t_c / 1e3) / 1e9 / HBM_PEAK_GBPS,
             "gather_weighted_us": t_w * 1e3,
             "gather_weighted_bytes_per_launch": w_bytes,
             "gather_weighted_frac": w_bytes / (t_w / 1e3) / 1e9 / HBM_PEAK_GBPS,
