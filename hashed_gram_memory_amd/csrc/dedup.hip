@@ -177,6 +177,23 @@ __device__ __forceinline__ uint32_t key_digit(uint64_t lo, uint64_t hi, int pass
     return static_cast<uint32_t>((pass < 8 ? lo >> (8 * pass) : hi >> (8 * (pass - 8)))) & 0xFFu;
 }
 
+// Add a wave's digits (digit `pass` of each valid lane's key) to the wave's
+// LDS histogram.  The lanes that share the first valid lane's digit are
+// added with one atomic: ids are skewed, so one digit is often most of the
+// wave (the high byte of a rank is mostly 0), and lane-by-lane atomics on one
+// LDS word serialise.
+__device__ __forceinline__ void count_digits(uint32_t* hist, uint64_t lo, uint64_t hi, int pass, bool valid,
+                                             uint32_t lane) {
+    const uint64_t live = __ballot(valid);
+    if (live == 0) return;
+    const uint32_t d = key_digit(lo, hi, pass);
+    const uint32_t leader = static_cast<uint32_t>(__ffsll(static_cast<long long>(live))) - 1u;
+    const uint32_t d0 = __builtin_amdgcn_readlane(d, leader);
+    const uint64_t same = __ballot(valid && d == d0);
+    if (lane == leader) atomicAdd(&hist[d0], static_cast<uint32_t>(__popcll(same)));
+    if (valid && d != d0) atomicAdd(&hist[d], 1u);
+}
+
 struct Workspace {
     Ctl* ctl;
     uint32_t* hist;    // [kMaxPasses][256] digit totals
@@ -471,9 +488,14 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
     __shared__ uint32_t wave_hist[kPassWaves][kRadix];  // counts per wave, then exclusive prefixes across waves
     __shared__ uint32_t next_hist[kPassWaves][kRadix];  // this tile's counts of the next pass's digit, per wave
     __shared__ uint32_t tile_cnt[kRadix];
+    __shared__ uint32_t tile_start[kRadix];  // where each digit's run starts within the tile's output order
     __shared__ uint32_t base[kRadix];  // where the tile's run of each digit starts in the output
-    __shared__ uint32_t wsum[kRadix / 64];
+    __shared__ uint32_t wsum[kRadix / 64], tsum[kRadix / 64];
     __shared__ uint32_t part[2][kGroupsOfRows][kStatusWords];  // earlier tiles' counts, per row group
+    // the tile's elements in output order, so that each digit's run is written by consecutive threads
+    __shared__ uint64_t stage_lo[kTile];
+    __shared__ uint64_t stage_hi[kTile];
+    __shared__ int32_t stage_val[kTile];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = threadIdx.x >> 6;
     const uint64_t lt = (uint64_t(1) << lane) - 1u;
@@ -542,10 +564,16 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
             run += c;
         }
         tile_cnt[dd] = run;
-        // exclusive scan of the pass's digit totals (threads 0..255 are waves 0..3)
+        // exclusive scans of the pass's digit totals and of this tile's digit counts (threads 0..255 are waves
+        // 0..3)
         const uint32_t x = wave_inclusive_scan(total);
-        if (lane == 63) wsum[wave] = x;
+        const uint32_t y = wave_inclusive_scan(run);
+        if (lane == 63) {
+            wsum[wave] = x;
+            tsum[wave] = y;
+        }
         base[dd] = x - total;
+        tile_start[dd] = y - run;
     }
     __syncthreads();
     // publish this tile's counts: word i holds digits 2i (low half) and 2i + 1 (high half)
@@ -556,9 +584,13 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
                      kPairReady | tile_cnt[2 * i] | (tile_cnt[2 * i + 1] << 16));
     }
     if (threadIdx.x < kRadix) {
-        uint32_t pre = 0;
-        for (uint32_t k = 0; k < wave; ++k) pre += wsum[k];
+        uint32_t pre = 0, tpre = 0;
+        for (uint32_t k = 0; k < wave; ++k) {
+            pre += wsum[k];
+            tpre += tsum[k];
+        }
         base[threadIdx.x] += pre;
+        tile_start[threadIdx.x] += tpre;
     }
     {  // counts in the earlier tiles: thread (g, i) sums word i of tiles g, g + 8, g + 16, ... below this one,
        // kLookAhead loads in flight (one round for up to 8 x kLookAhead earlier tiles)
@@ -576,7 +608,7 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
             if (!counted) {  // while the first loads are in flight: this tile's counts of the next digit
 #pragma unroll
                 for (uint32_t j = 0; j < kItems; ++j)
-                    if (first + j * 64u + lane < n) atomicAdd(&next_hist[wave][key_digit(lo[j], hi[j], pass + 1)], 1u);
+                    count_digits(next_hist[wave], lo[j], hi[j], pass + 1, first + j * 64u + lane < n, lane);
                 counted = true;
             }
 #pragma unroll
@@ -593,7 +625,7 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
         if (!counted) {  // no earlier tile for this thread to read
 #pragma unroll
             for (uint32_t j = 0; j < kItems; ++j)
-                if (first + j * 64u + lane < n) atomicAdd(&next_hist[wave][key_digit(lo[j], hi[j], pass + 1)], 1u);
+                count_digits(next_hist[wave], lo[j], hi[j], pass + 1, first + j * 64u + lane < n, lane);
         }
         part[0][g][i] = sum_lo;
         part[1][g][i] = sum_hi;
@@ -619,16 +651,38 @@ __global__ __launch_bounds__(kPassThreads) void pass_kernel(uint32_t n, int pass
     // Other tiles still scatter to positions below n.)
     if (s_failed) return;
 
+    // Stage the tile in output order: an element's place is where its digit's
+    // run starts in the tile plus its stable rank among the tile's elements of
+    // that digit.  Then thread i writes staged element i to the start of its
+    // digit's run in the output plus its place in the run, so each run is
+    // written by consecutive threads.
 #pragma unroll
     for (uint32_t j = 0; j < kItems; ++j) {
         const uint32_t i = first + j * 64u + lane;
         if (i < n) {
             const uint32_t d = key_digit(lo[j], hi[j], pass);
-            const uint32_t pos = base[d] + wave_hist[wave][d] + off[j];
+            const uint32_t at = tile_start[d] + wave_hist[wave][d] + off[j];
+            if (at < kTile) {
+                stage_lo[at] = lo[j];
+                if (has_hi) stage_hi[at] = hi[j];
+                stage_val[at] = v[j];
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t in_tile = min(kTile, n - tile * kTile);
+#pragma unroll
+    for (uint32_t j = 0; j < kItems; ++j) {
+        const uint32_t i = j * kPassThreads + threadIdx.x;
+        if (i < in_tile) {
+            const uint64_t klo = stage_lo[i];
+            const uint64_t khi = has_hi ? stage_hi[i] : 0u;
+            const uint32_t d = key_digit(klo, khi, pass);
+            const uint32_t pos = base[d] + (i - tile_start[d]);
             if (pos < n) {
-                lo_out[pos] = lo[j];
-                if (has_hi) hi_out[pos] = hi[j];
-                val_out[pos] = v[j];
+                lo_out[pos] = klo;
+                if (has_hi) hi_out[pos] = khi;
+                val_out[pos] = stage_val[i];
             }
         }
     }
