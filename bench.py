@@ -668,7 +668,8 @@ def main(argv=None) -> int:
                      else "engram_hash + engram_dedup + engram_gather_reduce (dedup mode)" if args.dedup
                      else "engram_hash + engram_gather_reduce_batched" if batched
                      else "engram_hash + engram_gather_reduce")
-                    + ("; batch i+1's hash (and dedup) on other streams while batch i is gathered" if pipelined
+                    + (("; batch i+1's dedup on another stream while batch i is looked up" if fused_dedup
+                        else "; batch i+1's hash (and dedup) on other streams while batch i is gathered") if pipelined
                        else "; all in order on one stream"),
             "n_unique": n_unique,
         },
@@ -702,7 +703,9 @@ def main(argv=None) -> int:
         "stage_timing": {"steps": n_stage, "us_per_step": stage_us,
                          "gather_ms": float(np.mean([e[4].elapsed_time(e[5]) for e in ev_stage])),
                          "note": "hash_ms and dedup_ms come from this separate run, with an event pair around every "
-                                 "stage; the timed steps record only the gather's pair"},
+                                 "stage; the timed steps record only the gather's pair"
+                                 + ("; pipelined, the stages on the side streams overlap the previous gather and their "
+                                    "times include waiting for the compute units it holds" if pipelined else "")},
         "us_per_step": ms_per_step * 1e3,
         "hash_gbps": None if hash_ms is None else HASH_BYTES_PER_TOKEN * n_tok / (hash_ms / 1e3) / 1e9,
         "gather_bytes_per_launch": gather_bytes,
