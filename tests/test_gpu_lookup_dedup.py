@@ -1,5 +1,5 @@
 """engram_lookup_dedup, the fused lookup over the groups engram_dedup wrote: against the oracle (small tables in
-every plan variant, and the full-size shared-prefix batch on sampled tokens), bitwise against the direct fused
+every plan variant; the decode, prefill and shared-prefix workloads at full size), bitwise against the direct fused
 lookup and the two-call path, with failed or out-of-range groups, and under HIP-graph replay."""
 import numpy as np
 import pytest
@@ -96,6 +96,31 @@ def test_lookup_dedup_shared_prefix_full_size_against_oracle():
     assert unwritten == 0, f"{unwritten} tokens never written"
     assert same
     assert nu < w.n_tok * 0.6
+    _, want, abs_sum = oracle_sampled(ids, hist, w.rows, w.table_seed, sample)
+    assert_within_tolerance(got, want, abs_sum)
+
+
+@pytest.mark.parametrize("key", [2, 3])
+def test_lookup_dedup_workloads_against_oracle(key):
+    """Decode (64 sequences x 1 token after a 3-token history, 2^20-row tables) and the 32K prefill (2^22-row
+    tables): every token written, bitwise the direct fused lookup, and against the oracle on all tokens (decode)
+    or 8,192 sampled ones (prefill)."""
+    w = workloads.WORKLOADS[key]
+    _say(f"lookup dedup, workload {key} n_tok={w.n_tok}")
+    ids, hist = workloads.make_ids(w)
+    t, c = device_tables(w.rows, w.table_seed)
+    plan = lib().Plan(t, c, vocab_size=workloads.VOCAB)
+    d_ids, d_hist = to_dev_ids(ids, hist)
+    groups = lib().dedup(plan, d_ids, d_hist)
+    out = torch.full((w.n_tok, 2, 256), float("nan"), dtype=torch.float32, device="cuda")
+    lib().lookup(plan, d_ids, d_hist, out=out, groups=groups)
+    direct = lib().lookup(plan, d_ids, d_hist)
+    torch.cuda.synchronize()
+    assert unwritten_tokens(out) == 0
+    assert torch.equal(out, direct)
+    assert int(groups.n_unique.item()) == oracle.dedup(oracle.windows(ids, hist))[2]
+    sample = batch_sample(w.n_seq, w.seq_len, 8192, 58 + key, seqs=(0, 1, w.n_seq - 1))
+    got = out[torch.from_numpy(sample).cuda()].cpu().numpy()
     _, want, abs_sum = oracle_sampled(ids, hist, w.rows, w.table_seed, sample)
     assert_within_tolerance(got, want, abs_sum)
 
