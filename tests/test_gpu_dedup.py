@@ -41,6 +41,30 @@ def test_dedup_groups_exact(n_seq, seq_len, hi, with_hist, vocab):
     _check_groups(groups, ids, hist)
 
 
+_VOCABS = (0, 7, 1000, 65536, 65537, 129280, 1 << 18, (1 << 18) + 1, 1 << 20)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_dedup_random_shapes(case):
+    """A seeded sweep over batch shapes, vocabulary sizes (both sides of the compacted-key range, and no bound),
+    id ranges from a handful of values (long runs of equal windows, skewed digits) to the whole vocabulary, with and
+    without history: groups exact against the oracle."""
+    rng = np.random.default_rng(9000 + case)
+    n_seq = int(rng.integers(1, 65))
+    seq_len = int(rng.integers(1, max(2, 60000 // n_seq)))
+    vocab = int(_VOCABS[case % len(_VOCABS)])
+    top = vocab if vocab else 1 << 31
+    hi = int(min(top, [3, 50, 5000, top][int(rng.integers(0, 4))]))
+    with_hist = bool(rng.integers(0, 2))
+    _say(f"dedup random case {case}: {n_seq}x{seq_len} ids<{hi} vocab={vocab} hist={with_hist}")
+    ids = rng.integers(0, hi, size=(n_seq, seq_len), dtype=np.int64).astype(np.int32)
+    hist = rng.integers(0, hi, size=(n_seq, 3), dtype=np.int64).astype(np.int32) if with_hist else None
+    plan = dummy_plan(4096, vocab)
+    groups = lib().dedup(plan, *to_dev_ids(ids, hist))
+    torch.cuda.synchronize()
+    _check_groups(groups, ids, hist)
+
+
 def test_dedup_shared_prefix_batch():
     """Sequences sharing a prefix collapse to one group per prefix position."""
     _say("dedup shared prefix 16 x (256 + 256)")
