@@ -287,3 +287,33 @@ def test_dedup_gives_up_safely_when_a_wait_is_cut_short(monkeypatch):
     groups = lib().dedup(plan, d_ids, workspace=ws)
     torch.cuda.synchronize()
     _check_groups(groups, ids, None)
+
+
+def _skewed_ids(pattern, rng, n_seq, seq_len):
+    if pattern == "one-window":  # every window (0, 0, 0, 0): a single group of all tokens
+        return np.zeros((n_seq, seq_len), dtype=np.int32)
+    if pattern == "two-ids":  # 16 windows, each repeated ~32,000 times
+        return rng.integers(0, 2, size=(n_seq, seq_len)).astype(np.int32)
+    if pattern == "heavy-plus-spread":  # 60% of ids one value: one window holds ~13% of tokens, the rest spread
+        ids = rng.integers(0, 129280, size=(n_seq, seq_len)).astype(np.int32)
+        ids[rng.random((n_seq, seq_len)) < 0.6] = 5
+        return ids
+    if pattern == "periodic":  # every sequence repeats one 97-token pattern: 97 windows, ~5,400 tokens each
+        base = rng.integers(0, 129280, size=97).astype(np.int32)
+        return np.tile(base, (n_seq, seq_len // 97 + 1))[:, :seq_len]
+    raise ValueError(pattern)
+
+
+@pytest.mark.parametrize("pattern", ["one-window", "two-ids", "heavy-plus-spread", "periodic"])
+def test_dedup_heavily_repeated_windows(pattern):
+    """64 x 8,192 tokens whose windows repeat heavily (one window; 16 windows; one window holding ~13% of the
+    tokens beside uniform ones; a 97-token period): a pass's digit is then one value for most of a tile, and
+    groups run to hundreds of thousands of members.  Groups exact against the oracle."""
+    n_seq, seq_len = 64, 8192
+    _say(f"dedup repeated windows {pattern} {n_seq}x{seq_len}")
+    rng = np.random.default_rng(len(pattern))
+    ids = _skewed_ids(pattern, rng, n_seq, seq_len)
+    plan = dummy_plan(4096, 129280)
+    groups = lib().dedup(plan, *to_dev_ids(ids, None))
+    torch.cuda.synchronize()
+    _check_groups(groups, ids, None)
