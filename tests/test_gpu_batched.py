@@ -135,3 +135,36 @@ def test_batched_across_the_chunk_boundary():
     want, abs_sum = oracle.gather_reduce(host_t, host_c, want_addr)
     assert_within_tolerance(batched_sample, want, abs_sum)
     assert np.array_equal(batched_sample, flat_sample)
+
+
+@pytest.mark.parametrize("route", ["lookup", "gather_batched", "lookup_dedup", "gather_dedup"])
+def test_batch_invariance_of_the_batch_paths(route):
+    """A sequence's vectors are bitwise the same whichever sequences share its batch, also on the paths where the
+    batch changes the visiting order (tiles of positions across sequences) or the work itself (dedup groups that
+    span sequences): the sequence alone, by the flat two calls, against the same sequence as row 4 of a 6-sequence
+    batch whose row 1 shares its first 300 ids and whose row 5 repeats it whole."""
+    _say(f"batch invariance through {route}")
+    R = 4096
+    host_t, host_c = workloads.dense_tables(557, R)
+    t, c = small_device_tables(host_t, host_c)
+    plan = lib().Plan(t, c, vocab_size=workloads.VOCAB)
+    rng = np.random.default_rng(3)
+    a = workloads.zipf_ids(rng, 700).reshape(1, 700)
+    batch = workloads.zipf_ids(rng, 6 * 700).reshape(6, 700)
+    batch[4] = a[0]
+    batch[5] = a[0]
+    batch[1, :300] = a[0, :300]
+    alone = lib().gather_reduce(plan, lib().hash(plan, *to_dev_ids(a, None)))
+    d_ids, _ = to_dev_ids(batch, None)
+    out = torch.full((batch.size, 2, 256), float("nan"), dtype=torch.float32, device="cuda")
+    if route == "lookup":
+        lib().lookup(plan, d_ids, out=out)
+    elif route == "gather_batched":
+        lib().gather_reduce_batched(plan, lib().hash(plan, d_ids), 6, out=out)
+    elif route == "lookup_dedup":
+        lib().lookup(plan, d_ids, out=out, groups=lib().dedup(plan, d_ids))
+    else:
+        lib().gather_reduce(plan, lib().hash(plan, d_ids), out=out, groups=lib().dedup(plan, d_ids))
+    torch.cuda.synchronize()
+    assert torch.equal(out[4 * 700:5 * 700], alone)
+    assert torch.equal(out[5 * 700:6 * 700], alone)
