@@ -70,6 +70,26 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
         limit = nu > 0 ? min(limit, static_cast<uint32_t>(nu)) : 0u;
     }
     if (item >= limit) return;
+
+    // Lane q < 24 hashes the module's row q = 8*(order-2) + head (lanes
+    // 24..63 repeat row 0) and owns that row in the lane-addressed loads.  Its
+    // lane-indexed parameters -- the 4 multipliers of its (order, head), its
+    // row count (and reciprocal), its table and scale bases -- are requested
+    // here, before the window ids, so that they take one memory round trip
+    // together while the wave-uniform id loads below are in flight.  A row of
+    // order n multiplies w_k for k < n only: the multiplier for k >= n is
+    // replaced by 0, with no branch between the loads.
+    const uint32_t s0 = m * kRowsPerModule;
+    const uint32_t mb = m * (kRowsPerModule * ENGRAM_MAX_ORDER);
+    const uint32_t q = owned_row(lane);
+    const uint32_t order = ENGRAM_MIN_ORDER + q / ENGRAM_N_HEADS;
+    uint64_t mk[ENGRAM_MAX_ORDER];
+#pragma unroll
+    for (uint32_t k = 0; k < ENGRAM_MAX_ORDER; ++k) mk[k] = P.h.mult[mb + q * ENGRAM_MAX_ORDER + k];
+    const uint64_t R = P.h.rows[s0 + q];
+    const uint64_t magic = POW2 ? 0u : P.h.magic[s0 + q];
+    const RowBases rb = row_bases(P.g, s0, lane);
+
     uint32_t seq, t, tok;
     if (kDedup) {
         // the group's first member; its position in its sequence gives the window
@@ -83,27 +103,35 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
         tok = batched_token(item, batch, &seq, &t);
     }
 
-    // Window of the token (wave-uniform): w[k] = id k positions back, else history, else 0.
+    // Window of the token (wave-uniform): w[k] = id k positions back, else
+    // history, else 0, each through the vocabulary map.  When the whole
+    // window lies inside the sequence (every position but the first 3), the
+    // 4 id loads, then the 4 map loads, are issued back to back.
     uint64_t w[ENGRAM_MAX_ORDER];
+    if (t >= ENGRAM_MAX_ORDER - 1) {
+        uint32_t v[ENGRAM_MAX_ORDER];
 #pragma unroll
-    for (int k = 0; k < ENGRAM_MAX_ORDER; ++k)
-        w[k] = window_id(ids, history, P.h.vocab_map, tok, seq, static_cast<int32_t>(t), k);
+        for (int k = 0; k < ENGRAM_MAX_ORDER; ++k) v[k] = static_cast<uint32_t>(ids[tok - k]);
+        const uint32_t* __restrict__ vmap = P.h.vocab_map;
+        if (vmap) {
+#pragma unroll
+            for (int k = 0; k < ENGRAM_MAX_ORDER; ++k) v[k] = vmap[v[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < ENGRAM_MAX_ORDER; ++k) w[k] = v[k];
+    } else {
+#pragma unroll
+        for (int k = 0; k < ENGRAM_MAX_ORDER; ++k)
+            w[k] = window_id(ids, history, P.h.vocab_map, tok, seq, static_cast<int32_t>(t), k);
+    }
 
-    // Lane q < 24 hashes the module's row q = 8*(order-2) + head (lanes
-    // 24..63 repeat row 0) and keeps the address for the lane-addressed loads.
-    const uint32_t s0 = m * kRowsPerModule;
-    const uint32_t mb = m * (kRowsPerModule * ENGRAM_MAX_ORDER);
-    const uint32_t q = owned_row(lane);
-    const uint32_t order = ENGRAM_MIN_ORDER + q / ENGRAM_N_HEADS;
     uint64_t x = 0;
 #pragma unroll
-    for (uint32_t k = 0; k < ENGRAM_MAX_ORDER; ++k)
-        if (k < order) x ^= w[k] * P.h.mult[mb + q * ENGRAM_MAX_ORDER + k];
-    const uint64_t R = P.h.rows[s0 + q];
-    const uint32_t a = POW2 ? static_cast<uint32_t>(x & (R - 1u)) : mod_rows(x, R, P.h.magic[s0 + q]);
+    for (uint32_t k = 0; k < ENGRAM_MAX_ORDER; ++k) x ^= w[k] * (k < order ? mk[k] : 0u);
+    const uint32_t a = POW2 ? static_cast<uint32_t>(x & (R - 1u)) : mod_rows(x, R, magic);
 
     RowSet r;
-    load_rows<FMT>(P.g, s0, a, lane, r);
+    load_rows_at<FMT>(rb, a, lane, r);
     const f32x4 acc = sum_rows<FMT>(r, lane);
     const size_t col = static_cast<size_t>(m) * kRowBytes + lane * 4u;
     if (!kDedup) {

@@ -64,13 +64,23 @@ struct RowSet {
     uint32_t s_hi[kRowsPerModule];  //   E8M0 bytes 4..7
 };
 
-// `a`: this lane's address, the row of sub-table s0 + owned_row(lane).
-template <int FMT>
-__device__ __forceinline__ void load_rows(const GatherParams& P, uint32_t s0, uint32_t a, uint32_t lane, RowSet& r) {
+// Table and scale base pointers of the sub-table whose row this lane owns
+// (s0 + owned_row(lane)): lane-indexed loads from the plan's pointer arrays,
+// which a kernel can request early, before the row address is known.
+struct RowBases {
+    uint64_t tab, sc;
+};
+__device__ __forceinline__ RowBases row_bases(const GatherParams& P, uint32_t s0, uint32_t lane) {
     const uint32_t q = owned_row(lane);
+    return RowBases{reinterpret_cast<uint64_t>(P.tab[s0 + q]), reinterpret_cast<uint64_t>(P.sc[s0 + q])};
+}
+
+// `a`: this lane's address, the row of its sub-table (bases from row_bases).
+template <int FMT>
+__device__ __forceinline__ void load_rows_at(const RowBases& rb, uint32_t a, uint32_t lane, RowSet& r) {
     constexpr uint64_t kScaleBytes = FMT == ENGRAM_SCALE_F32_ROW ? 4u : 8u;
-    const uint64_t base = reinterpret_cast<uint64_t>(P.tab[s0 + q]) + static_cast<uint64_t>(a) * kRowBytes;
-    const uint64_t sadr = reinterpret_cast<uint64_t>(P.sc[s0 + q]) + static_cast<uint64_t>(a) * kScaleBytes;
+    const uint64_t base = rb.tab + static_cast<uint64_t>(a) * kRowBytes;
+    const uint64_t sadr = rb.sc + static_cast<uint64_t>(a) * kScaleBytes;
     const uint32_t base_lo = static_cast<uint32_t>(base), base_hi = static_cast<uint32_t>(base >> 32);
     const uint32_t sadr_lo = static_cast<uint32_t>(sadr), sadr_hi = static_cast<uint32_t>(sadr >> 32);
 #pragma unroll
@@ -97,6 +107,12 @@ __device__ __forceinline__ void load_rows(const GatherParams& P, uint32_t s0, ui
         // pointers are live in scalar registers
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// `a`: this lane's address, the row of sub-table s0 + owned_row(lane).
+template <int FMT>
+__device__ __forceinline__ void load_rows(const GatherParams& P, uint32_t s0, uint32_t a, uint32_t lane, RowSet& r) {
+    load_rows_at<FMT>(row_bases(P, s0, lane), a, lane, r);
 }
 
 // Scale of row k for this lane's 4 elements.
