@@ -81,13 +81,22 @@ __global__ __launch_bounds__(256) void gather_reduce_kernel(const GatherParams P
         // first store is unconditional; a loop that could run zero times
         // would let the compiler sink the loads below a branch that the
         // row-base broadcasts cannot follow, keeping all 24 live at once.
+        // The members' indices are read 64 at a time, one per lane, and
+        // broadcast one by one, so a group shared by many sequences costs one
+        // load per 64 members instead of a dependent load before every store.
         uint32_t i = static_cast<uint32_t>(offsets[item]);
         const uint32_t end = min(static_cast<uint32_t>(offsets[item + 1]), n_tok);
         do {
-            const uint32_t t = static_cast<uint32_t>(perm[i]);
-            if (t < n_tok)
-                __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(t) * (2 * kRowBytes) + col));
-        } while (++i < end);
+            const uint32_t cnt = min(64u, end - i);
+            const uint32_t mine = lane < cnt ? static_cast<uint32_t>(perm[i + lane]) : n_tok;
+            uint32_t j = 0;
+            do {
+                const uint32_t t = static_cast<uint32_t>(__builtin_amdgcn_readlane(mine, j));
+                if (t < n_tok)
+                    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(t) * (2 * kRowBytes) + col));
+            } while (++j < cnt);
+            i += cnt;
+        } while (i < end);
     }
 }
 

@@ -137,15 +137,24 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
     if (!kDedup) {
         __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + col));
     } else {
-        // every group has a member (the token above): the first store is
-        // unconditional, as in gather_reduce_kernel's dedup mode
+        // Every group has a member (the token above), so the first store is
+        // unconditional, as in gather_reduce_kernel's dedup mode.  The
+        // members' indices are read 64 at a time, one per lane, and broadcast
+        // one by one: a group shared by many sequences costs one load per 64
+        // members instead of a dependent load before every store.
         uint32_t i = static_cast<uint32_t>(T.offsets[item]);
         const uint32_t end = min(static_cast<uint32_t>(T.offsets[item + 1]), T.n_tok);
         do {
-            const uint32_t u = static_cast<uint32_t>(T.perm[i]);
-            if (u < T.n_tok)
-                __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(u) * (2 * kRowBytes) + col));
-        } while (++i < end);
+            const uint32_t cnt = min(64u, end - i);
+            const uint32_t mine = lane < cnt ? static_cast<uint32_t>(T.perm[i + lane]) : T.n_tok;
+            uint32_t j = 0;
+            do {
+                const uint32_t u = static_cast<uint32_t>(__builtin_amdgcn_readlane(mine, j));
+                if (u < T.n_tok)
+                    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(u) * (2 * kRowBytes) + col));
+            } while (++j < cnt);
+            i += cnt;
+        } while (i < end);
     }
 }
 
