@@ -1,17 +1,19 @@
 // Visiting order for a batch of sequences, shared by the fused lookup and
 // the batched gather.
 //
-// Items (one per token) are visited in tiles of `tile` positions (64, or the
-// whole sequence if shorter); within a tile, sequence by sequence.
-// Consecutive items are consecutive positions of one sequence, so a wave's
-// neighbours write neighbouring outputs, and the same position of the next
-// sequence comes `tile` items later: 32 blocks of 4 items x 2 modules for a
-// 64-position tile, which the round-robin dispatcher (block b to XCD b % 8)
-// sends to the same XCD.  Sequences that share a prefix therefore read each
-// prefix row from that XCD's L2 after its first fetch.  With one sequence
-// the order is plain token order.  Measured tile widths on 64 sequences
-// sharing a 4,096-token prefix (fused lookup): 32 positions 1.02x, 128 1.04x,
-// 256 1.12x the time of 64.
+// A block (4 waves, one module) takes G sequences at 4/G consecutive
+// positions, G = 4, 2 or 1 (batch_order below picks it from the sequence
+// count).  Blocks go in tiles of `tile` positions (64, or the whole sequence
+// if shorter); within a tile, group of G sequences by group, and within a
+// group by position.  The same positions of the next group come one group's
+// blocks later: 64 blocks x 2 modules for G = 4 and a 64-position tile, a
+// multiple of 8, so the round-robin dispatcher (block b to XCD b % 8) sends
+// them to the same XCD.  Sequences that share a prefix therefore find each
+// prefix row in that XCD's L2 after its first fetch, and within a block the
+// kernels go further: a wave whose 24 addresses equal an earlier wave's of
+// the same block takes that wave's sum through LDS instead of gathering the
+// rows again.  With one sequence (G = 1) a block is 4 consecutive tokens and
+// the order is plain token order.
 #pragma once
 
 #include "engram_internal.h"
@@ -19,25 +21,75 @@
 namespace engram {
 
 constexpr uint32_t kBatchTile = 64;
+constexpr uint32_t kBlockWaves = 4;
 
 struct BatchOrder {
-    uint32_t n_seq, seq_len, tile;  // tile = min(kBatchTile, seq_len), so tile * n_seq <= n_tok
+    uint32_t n_seq, seq_len, tile;  // tile = min(kBatchTile, seq_len)
+    uint32_t gshift;                // G = 1 << gshift sequences per block
+    uint32_t n_groups;              // ceil(n_seq / G)
+    uint32_t full_tiles;            // tiles of `tile` positions
+    uint32_t last;                  // positions in the partial last tile, 0 if none
+    uint32_t tile_blocks;           // blocks per full tile (per module)
+    uint32_t n_blocks;              // blocks per module in all
 };
 
-inline BatchOrder batch_order(uint32_t n_tok, uint32_t seq_len) {
-    return BatchOrder{n_tok / seq_len, seq_len, seq_len < kBatchTile ? seq_len : kBatchTile};
+// Sequences per block: the largest of 4 and 2 whose idle waves (G * groups -
+// n_seq) are at most 1/8 of the sequences, else 1.
+inline uint32_t batch_gshift(uint32_t n_seq) {
+    for (uint32_t sh = 2; sh > 0; --sh) {
+        const uint32_t g = 1u << sh;
+        const uint64_t idle = uint64_t((n_seq + g - 1) / g) * g - n_seq;
+        if (idle * 8u <= n_seq) return sh;
+    }
+    return 0;
 }
 
-// Token index of `item`; its sequence and position in *seq and *t.
-__device__ __forceinline__ uint32_t batched_token(uint32_t item, const BatchOrder& o, uint32_t* seq, uint32_t* t) {
-    const uint32_t span = o.tile * o.n_seq;  // items per tile of positions
-    const uint32_t tile_idx = item / span;
-    const uint32_t p0 = tile_idx * o.tile;
-    const uint32_t width = min(o.tile, o.seq_len - p0);  // the last tile may be narrower
-    const uint32_t rem = item - tile_idx * span;
-    *seq = rem / width;
-    *t = p0 + (rem - *seq * width);
-    return *seq * o.seq_len + *t;
+inline BatchOrder batch_order(uint32_t n_tok, uint32_t seq_len) {
+    BatchOrder o;
+    o.n_seq = n_tok / seq_len;
+    o.seq_len = seq_len;
+    o.tile = seq_len < kBatchTile ? seq_len : kBatchTile;
+    o.gshift = batch_gshift(o.n_seq);
+    const uint32_t per = kBlockWaves >> o.gshift;  // positions per block
+    o.n_groups = (o.n_seq + (1u << o.gshift) - 1u) >> o.gshift;
+    o.full_tiles = seq_len / o.tile;
+    o.last = seq_len - o.full_tiles * o.tile;
+    o.tile_blocks = o.n_groups * ((o.tile + per - 1u) / per);
+    o.n_blocks = o.full_tiles * o.tile_blocks + o.n_groups * ((o.last + per - 1u) / per);
+    return o;
+}
+
+// Sequence and position of wave `wave` of block `blk` (< o.n_blocks); *valid
+// is false for the idle waves of a partial group or a narrow last tile.
+__device__ __forceinline__ void block_token(uint32_t blk, uint32_t wave, const BatchOrder& o, uint32_t* seq,
+                                            uint32_t* t, bool* valid) {
+    uint32_t tile_idx = o.full_tiles, rem, width = o.last;
+    if (blk < o.full_tiles * o.tile_blocks) {
+        tile_idx = blk / o.tile_blocks;
+        width = o.tile;
+    }
+    rem = blk - tile_idx * o.tile_blocks;
+    const uint32_t per = kBlockWaves >> o.gshift;
+    const uint32_t bpg = (width + per - 1u) / per;  // blocks per group in this tile
+    const uint32_t g = rem / bpg;
+    const uint32_t q = rem - g * bpg;
+    const uint32_t s = (g << o.gshift) + (wave & ((1u << o.gshift) - 1u));
+    const uint32_t p = q * per + (wave >> o.gshift);
+    *valid = s < o.n_seq && p < width;
+    *seq = s;
+    *t = tile_idx * o.tile + p;
+}
+
+// The first valid wave of the block, before this one, whose 24 addresses
+// (lane q < 24 holds address q; lanes 24..63 repeat address 0) equal this
+// wave's, or this wave itself.  sa and sval hold every wave's addresses and
+// validity in LDS; call after the barrier that follows their writes.
+__device__ __forceinline__ uint32_t first_equal_wave(const uint32_t (*sa)[kRowsPerModule], const uint32_t* sval,
+                                                     uint32_t wave, uint32_t lane, uint32_t a) {
+    const uint32_t q = lane < kRowsPerModule ? lane : 0u;
+    for (uint32_t u = 0; u < wave; ++u)
+        if (sval[u] && __ballot(lane < kRowsPerModule && sa[u][q] != a) == 0) return u;
+    return wave;
 }
 
 // The batched gather: engram_gather_reduce (direct mode) over n_seq x seq_len

@@ -6,52 +6,88 @@
 // a prefix then read the same rows in every sequence, and this order lets one
 // XCD's L2 serve the repeats.  Per token the work, and so the result, is that
 // of gather_reduce_kernel: the same loader and fused multiply-add sequence.
+//
+// With several sequences per block (kShare), the 4 waves of a block are the
+// same position of consecutive sequences.  Each posts its 24 addresses in
+// LDS; a wave whose addresses equal an earlier wave's does not gather but
+// takes that wave's sum from LDS after a barrier, since equal addresses give
+// the same rows and so the same sum.  A prefix shared by the batch is then
+// gathered once per block of sequences instead of once per sequence.
 #include "batch_order.h"
 #include "row_sum.h"
 
 namespace engram {
 namespace {
 
-template <int FMT>
+template <int FMT, bool kShare>
 __global__ __launch_bounds__(256) void gather_batched_kernel(const GatherParams P, const uint32_t* __restrict__ addr,
-                                                             uint32_t item_base, uint32_t item_end, BatchOrder batch,
+                                                             uint32_t blk_base, BatchOrder o,
                                                              float* __restrict__ out) {
-    const uint32_t b = blockIdx.x;
-    const uint32_t module = b & 1u;  // block b: module b % 2 of 4 consecutive items
-    const uint32_t group = b >> 1;
+    const uint32_t module = blockIdx.x & 1u;  // block b: module b % 2 of batch-order block b / 2
+    const uint32_t blk = blk_base + (blockIdx.x >> 1);
+    if (blk >= o.n_blocks) return;  // the whole block
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t item = item_base + group * 4u + wave;
-    if (item >= item_end) return;
     uint32_t seq, t;
-    const uint32_t tok = batched_token(item, batch, &seq, &t);
-
+    bool valid;
+    block_token(blk, wave, o, &seq, &t, &valid);
+    // an idle wave reads token 0's addresses (in bounds) and stores nothing
+    const size_t tok = valid ? static_cast<size_t>(seq) * o.seq_len + t : 0u;
     const uint32_t s0 = module * kRowsPerModule;
-    const uint32_t a = addr[static_cast<size_t>(tok) * kSub + s0 + owned_row(lane)];
-    RowSet r;
-    load_rows<FMT>(P, s0, a, lane, r);
-    const f32x4 acc = sum_rows<FMT>(r, lane);
-    __builtin_nontemporal_store(
-        acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + module * kRowBytes + lane * 4u));
+    const uint32_t a = addr[tok * kSub + s0 + owned_row(lane)];
+    f32x4* dst = reinterpret_cast<f32x4*>(out + tok * (2 * kRowBytes) + module * kRowBytes + lane * 4u);
+    if (!kShare) {
+        if (!valid) return;
+        RowSet r;
+        load_rows<FMT>(P, s0, a, lane, r);
+        __builtin_nontemporal_store(sum_rows<FMT>(r, lane), dst);
+        return;
+    }
+    __shared__ uint32_t sa[kBlockWaves][kRowsPerModule];
+    __shared__ uint32_t sval[kBlockWaves];
+    __shared__ f32x4 sacc[kBlockWaves][64];
+    const RowBases rb = row_bases(P, s0, lane);
+    if (lane < kRowsPerModule) sa[wave][lane] = a;
+    if (lane == 0) sval[wave] = valid ? 1u : 0u;
+    __syncthreads();
+    const uint32_t src = valid ? first_equal_wave(sa, sval, wave, lane, a) : kBlockWaves;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (src == wave) {
+        RowSet r;
+        load_rows_at<FMT>(rb, a, lane, r);
+        acc = sum_rows<FMT>(r, lane);
+        sacc[wave][lane] = acc;
+    }
+    __syncthreads();
+    if (!valid) return;
+    if (src != wave) acc = sacc[src][lane];
+    __builtin_nontemporal_store(acc, dst);
+}
+
+template <int FMT>
+void launch_one(const GatherParams& p, const uint32_t* addr, uint32_t base, uint32_t nb, const BatchOrder& o,
+                float* out, hipStream_t stream) {
+    if (o.gshift > 0)
+        hipLaunchKernelGGL((gather_batched_kernel<FMT, true>), dim3(2u * nb), dim3(256), 0, stream, p, addr, base, o,
+                           out);
+    else
+        hipLaunchKernelGGL((gather_batched_kernel<FMT, false>), dim3(2u * nb), dim3(256), 0, stream, p, addr, base, o,
+                           out);
 }
 
 }  // namespace
 
 hipError_t launch_gather_batched(const GatherParams& p, const uint32_t* addr, uint32_t n_tok, uint32_t seq_len,
                                  float* out, hipStream_t stream) {
-    // Launches cover at most 2^24 items so the grid stays far below 2^32 threads.
-    constexpr uint32_t kChunk = 1u << 24;
-    const BatchOrder batch = batch_order(n_tok, seq_len);
-    for (uint32_t base = 0; base < n_tok; base += kChunk) {
-        const uint32_t n = min(kChunk, n_tok - base);
-        const uint32_t groups = ((n + 3u) / 4u + 3u) & ~3u;
-        const dim3 grid(2u * groups), block(256);
+    // Launches cover at most 2^22 blocks per module, so the grid stays below 2^31 threads.
+    constexpr uint32_t kChunkBlocks = 1u << 22;
+    const BatchOrder o = batch_order(n_tok, seq_len);
+    for (uint32_t base = 0; base < o.n_blocks; base += kChunkBlocks) {
+        const uint32_t nb = min(kChunkBlocks, o.n_blocks - base);
         if (p.scale_format == ENGRAM_SCALE_E8M0_BLOCK32)
-            hipLaunchKernelGGL((gather_batched_kernel<ENGRAM_SCALE_E8M0_BLOCK32>), grid, block, 0, stream, p, addr, base,
-                               base + n, batch, out);
+            launch_one<ENGRAM_SCALE_E8M0_BLOCK32>(p, addr, base, nb, o, out, stream);
         else
-            hipLaunchKernelGGL((gather_batched_kernel<ENGRAM_SCALE_F32_ROW>), grid, block, 0, stream, p, addr, base,
-                               base + n, batch, out);
+            launch_one<ENGRAM_SCALE_F32_ROW>(p, addr, base, nb, o, out, stream);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -52,24 +52,35 @@ struct Tokens {
     const int32_t* n_unique;
 };
 
-template <bool POW2, int FMT, bool kDedup>
-__global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const Tokens T, uint32_t item_base,
+// How a launch maps blocks to tokens: the batch order of batch_order.h with
+// one sequence per block (kTokens) or several, sharing equal sums through LDS
+// (kShared); or one wave per dedup group (kGroups).
+enum { kTokens = 0, kShared = 1, kGroups = 2 };
+
+template <bool POW2, int FMT, int MODE>
+__global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const Tokens T, uint32_t base,
                                                      uint32_t item_end, BatchOrder batch, float* __restrict__ out) {
     const int32_t* __restrict__ ids = T.ids;
     const int32_t* __restrict__ history = T.history;
-    const uint32_t b = blockIdx.x;
-    const uint32_t m = b & 1u;  // block b: module b % 2 of 4 consecutive items
-    const uint32_t group = b >> 1;
+    const uint32_t m = blockIdx.x & 1u;  // block b: module b % 2
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t item = item_base + group * 4u + wave;
 
-    uint32_t limit = item_end;
-    if (kDedup) {
+    uint32_t item = 0;  // kGroups: the group
+    bool valid = true;  // kShared: an idle wave of a partial block still takes part in its barriers
+    uint32_t seq = 0, t = 0;
+    if (MODE == kGroups) {
+        item = base + (blockIdx.x >> 1) * kBlockWaves + wave;
         const int32_t nu = *T.n_unique;  // negative: the dedup call failed, there are no groups
-        limit = nu > 0 ? min(limit, static_cast<uint32_t>(nu)) : 0u;
+        const uint32_t limit = nu > 0 ? min(item_end, static_cast<uint32_t>(nu)) : 0u;
+        if (item >= limit) return;
+    } else {
+        const uint32_t blk = base + (blockIdx.x >> 1);
+        if (blk >= batch.n_blocks) return;  // the whole block
+        block_token(blk, wave, batch, &seq, &t, &valid);
+        if (MODE == kTokens && !valid) return;
+        if (!valid) seq = t = 0;  // an idle wave works on token 0 and stores nothing
     }
-    if (item >= limit) return;
 
     // Lane q < 24 hashes the module's row q = 8*(order-2) + head (lanes
     // 24..63 repeat row 0) and owns that row in the lane-addressed loads.  Its
@@ -90,8 +101,8 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
     const uint64_t magic = POW2 ? 0u : P.h.magic[s0 + q];
     const RowBases rb = row_bases(P.g, s0, lane);
 
-    uint32_t seq, t, tok;
-    if (kDedup) {
+    uint32_t tok;
+    if (MODE == kGroups) {
         // the group's first member; its position in its sequence gives the window
         const uint32_t first = static_cast<uint32_t>(T.offsets[item]);
         if (first >= T.n_tok) return;
@@ -100,7 +111,7 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
         seq = tok / batch.seq_len;
         t = tok - seq * batch.seq_len;
     } else {
-        tok = batched_token(item, batch, &seq, &t);
+        tok = seq * batch.seq_len + t;
     }
 
     // Window of the token (wave-uniform): w[k] = id k positions back, else
@@ -130,11 +141,34 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
     for (uint32_t k = 0; k < ENGRAM_MAX_ORDER; ++k) x ^= w[k] * (k < order ? mk[k] : 0u);
     const uint32_t a = POW2 ? static_cast<uint32_t>(x & (R - 1u)) : mod_rows(x, R, magic);
 
+    const size_t col = static_cast<size_t>(m) * kRowBytes + lane * 4u;
+    if (MODE == kShared) {
+        // as gather_batched_kernel: a wave whose 24 addresses equal an earlier
+        // wave's of the block takes that wave's sum instead of gathering
+        __shared__ uint32_t sa[kBlockWaves][kRowsPerModule];
+        __shared__ uint32_t sval[kBlockWaves];
+        __shared__ f32x4 sacc[kBlockWaves][64];
+        if (lane < kRowsPerModule) sa[wave][lane] = a;
+        if (lane == 0) sval[wave] = valid ? 1u : 0u;
+        __syncthreads();
+        const uint32_t src = valid ? first_equal_wave(sa, sval, wave, lane, a) : kBlockWaves;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (src == wave) {
+            RowSet r;
+            load_rows_at<FMT>(rb, a, lane, r);
+            acc = sum_rows<FMT>(r, lane);
+            sacc[wave][lane] = acc;
+        }
+        __syncthreads();
+        if (!valid) return;
+        if (src != wave) acc = sacc[src][lane];
+        __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + col));
+        return;
+    }
     RowSet r;
     load_rows_at<FMT>(rb, a, lane, r);
     const f32x4 acc = sum_rows<FMT>(r, lane);
-    const size_t col = static_cast<size_t>(m) * kRowBytes + lane * 4u;
-    if (!kDedup) {
+    if (MODE == kTokens) {
         __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + col));
     } else {
         // Every group has a member (the token above), so the first store is
@@ -159,12 +193,17 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
 }
 
 template <bool POW2, int FMT>
-void launch_one(const LookupParams& p, const Tokens& tk, dim3 grid, uint32_t base, uint32_t end,
+void launch_one(const LookupParams& p, const Tokens& tk, uint32_t grid, uint32_t base, uint32_t end,
                 const BatchOrder& batch, float* out, hipStream_t stream) {
     if (tk.perm)
-        hipLaunchKernelGGL((lookup_kernel<POW2, FMT, true>), grid, dim3(256), 0, stream, p, tk, base, end, batch, out);
+        hipLaunchKernelGGL((lookup_kernel<POW2, FMT, kGroups>), dim3(grid), dim3(256), 0, stream, p, tk, base, end,
+                           batch, out);
+    else if (batch.gshift > 0)
+        hipLaunchKernelGGL((lookup_kernel<POW2, FMT, kShared>), dim3(grid), dim3(256), 0, stream, p, tk, base, end,
+                           batch, out);
     else
-        hipLaunchKernelGGL((lookup_kernel<POW2, FMT, false>), grid, dim3(256), 0, stream, p, tk, base, end, batch, out);
+        hipLaunchKernelGGL((lookup_kernel<POW2, FMT, kTokens>), dim3(grid), dim3(256), 0, stream, p, tk, base, end,
+                           batch, out);
 }
 
 }  // namespace
@@ -178,15 +217,16 @@ hipError_t launch_lookup(const HashParams& h, const GatherParams& g, const int32
     const Tokens tk{ids, history, n_tok, perm, offsets, n_unique};
     bool pow2 = true;
     for (int s = 0; s < kSub; ++s) pow2 = pow2 && (h.rows[s] & (h.rows[s] - 1u)) == 0;
-    // Launches cover at most 2^24 items (tokens, or groups in dedup mode) so
-    // the grid stays far below 2^32 threads.
-    constexpr uint32_t kChunk = 1u << 24;
+    // Dedup mode launches cover at most 2^24 groups, 4 per block; the batch
+    // order at most 2^22 blocks (per module): either way the grid stays below
+    // 2^31 threads.
     const bool mx = g.scale_format == ENGRAM_SCALE_E8M0_BLOCK32;
     const BatchOrder batch = batch_order(n_tok, seq_len);
-    for (uint32_t base = 0; base < n_tok; base += kChunk) {
-        const uint32_t n = min(kChunk, n_tok - base);
-        const uint32_t groups = ((n + 3u) / 4u + 3u) & ~3u;
-        const dim3 grid(2u * groups);
+    const uint32_t total = perm ? n_tok : batch.n_blocks;
+    const uint32_t step = perm ? (1u << 24) : (1u << 22);
+    for (uint32_t base = 0; base < total; base += step) {
+        const uint32_t n = min(step, total - base);
+        const uint32_t grid = perm ? 2u * (((n + 3u) / 4u + 3u) & ~3u) : 2u * n;
         if (pow2 && mx)
             launch_one<true, ENGRAM_SCALE_E8M0_BLOCK32>(p, tk, grid, base, base + n, batch, out, stream);
         else if (pow2)

@@ -21,6 +21,9 @@ def _say(msg):
 @pytest.mark.parametrize("fmt", ["f32_row", "e8m0_block32"])
 @pytest.mark.parametrize("n_seq,seq_len,shared", [
     (1, 1000, 0), (3, 5, 0), (5, 77, 30), (64, 300, 128), (2, 64, 64), (7, 129, 0), (64, 1, 0),
+    # 2 sequences per block, one idle wave; 4 per block, three idle; idle
+    # positions in a narrow tile; every sequence equal
+    (9, 70, 40), (33, 67, 50), (6, 3, 3), (10, 67, 20), (4, 130, 130),
 ])
 def test_batched_equals_flat(fmt, n_seq, seq_len, shared):
     _say(f"batched gather {n_seq}x{seq_len} shared={shared} {fmt}")
@@ -38,6 +41,32 @@ def test_batched_equals_flat(fmt, n_seq, seq_len, shared):
     batched = torch.full_like(flat, float("nan"))
     lib().gather_reduce_batched(plan, addr, n_seq, out=batched)
     fused = lib().lookup(plan, d_ids)
+    torch.cuda.synchronize()
+    assert torch.equal(batched, flat)
+    assert torch.equal(fused, flat)
+
+
+@pytest.mark.parametrize("n_seq", [8, 10])
+def test_batched_partial_sharing_within_blocks(n_seq):
+    """Sequences equal to a later, not the first, sequence of their block, and
+    equal over part of their length only: every wave must take the sum of the
+    first equal wave or gather its own."""
+    _say(f"batched gather + fused lookup, {n_seq} sequences with scattered duplicates")
+    t, c = small_device_tables(*workloads.dense_tables(32, 4096, "f32_row"))
+    plan = lib().Plan(t, c)
+    rng = np.random.default_rng(700 + n_seq)
+    ids = rng.integers(0, 129280, size=(n_seq, 150)).astype(np.int32)
+    ids[2] = ids[1]
+    ids[3, :75] = ids[0, :75]
+    ids[7, 40:] = ids[5, 40:]
+    ids[6, ::2] = ids[4, ::2]
+    d_ids, _ = to_dev_ids(ids, None)
+    addr = lib().hash(plan, d_ids)
+    flat = lib().gather_reduce(plan, addr)
+    batched = torch.full_like(flat, float("nan"))
+    lib().gather_reduce_batched(plan, addr, n_seq, out=batched)
+    fused = torch.full_like(flat, float("nan"))
+    lib().lookup(plan, d_ids, out=fused)
     torch.cuda.synchronize()
     assert torch.equal(batched, flat)
     assert torch.equal(fused, flat)
