@@ -22,10 +22,16 @@ namespace engram {
 
 constexpr uint32_t kBatchTile = 64;
 constexpr uint32_t kBlockWaves = 4;
+// Sharing sums within a block costs two barriers, so a wave's stores wait for
+// the slowest gather of its block.  A launch of a few thousand tokens fits
+// the chip at once (two waves per token; 256 CUs hold 8,192 waves) and is
+// bound by that latency, so only batches of at least this many tokens share.
+constexpr uint32_t kShareMinTokens = 8192;
 
 struct BatchOrder {
     uint32_t n_seq, seq_len, tile;  // tile = min(kBatchTile, seq_len)
     uint32_t gshift;                // G = 1 << gshift sequences per block
+    uint32_t share;                 // 1: equal-address waves share one gather
     uint32_t n_groups;              // ceil(n_seq / G)
     uint32_t full_tiles;            // tiles of `tile` positions
     uint32_t last;                  // positions in the partial last tile, 0 if none
@@ -50,6 +56,7 @@ inline BatchOrder batch_order(uint32_t n_tok, uint32_t seq_len) {
     o.seq_len = seq_len;
     o.tile = seq_len < kBatchTile ? seq_len : kBatchTile;
     o.gshift = batch_gshift(o.n_seq);
+    o.share = o.gshift > 0 && n_tok >= kShareMinTokens ? 1u : 0u;
     const uint32_t per = kBlockWaves >> o.gshift;  // positions per block
     o.n_groups = (o.n_seq + (1u << o.gshift) - 1u) >> o.gshift;
     o.full_tiles = seq_len / o.tile;

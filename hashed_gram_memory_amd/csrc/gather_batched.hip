@@ -7,7 +7,7 @@
 // XCD's L2 serve the repeats.  Per token the work, and so the result, is that
 // of gather_reduce_kernel: the same loader and fused multiply-add sequence.
 //
-// With several sequences per block (kShare), the 4 waves of a block are the
+// With several sequences per block in a large batch (kShare), the 4 waves of a block are the
 // same position of consecutive sequences.  Each posts its 24 addresses in
 // LDS; a wave whose addresses equal an earlier wave's does not gather but
 // takes that wave's sum from LDS after a barrier, since equal addresses give
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void gather_batched_kernel(const GatherParams 
 template <int FMT>
 void launch_one(const GatherParams& p, const uint32_t* addr, uint32_t base, uint32_t nb, const BatchOrder& o,
                 float* out, hipStream_t stream) {
-    if (o.gshift > 0)
+    if (o.share)
         hipLaunchKernelGGL((gather_batched_kernel<FMT, true>), dim3(2u * nb), dim3(256), 0, stream, p, addr, base, o,
                            out);
     else

@@ -52,9 +52,10 @@ struct Tokens {
     const int32_t* n_unique;
 };
 
-// How a launch maps blocks to tokens: the batch order of batch_order.h with
-// one sequence per block (kTokens) or several, sharing equal sums through LDS
-// (kShared); or one wave per dedup group (kGroups).
+// How a launch maps blocks to tokens: the batch order of batch_order.h,
+// each wave gathering for itself (kTokens) or waves with equal addresses
+// sharing one gather through LDS (kShared); or one wave per dedup group
+// (kGroups).
 enum { kTokens = 0, kShared = 1, kGroups = 2 };
 
 template <bool POW2, int FMT, int MODE>
@@ -198,7 +199,7 @@ void launch_one(const LookupParams& p, const Tokens& tk, uint32_t grid, uint32_t
     if (tk.perm)
         hipLaunchKernelGGL((lookup_kernel<POW2, FMT, kGroups>), dim3(grid), dim3(256), 0, stream, p, tk, base, end,
                            batch, out);
-    else if (batch.gshift > 0)
+    else if (batch.share)
         hipLaunchKernelGGL((lookup_kernel<POW2, FMT, kShared>), dim3(grid), dim3(256), 0, stream, p, tk, base, end,
                            batch, out);
     else

@@ -228,8 +228,10 @@ int engram_gather_reduce(engram_plan_t plan, const uint32_t* addr, int64_t n_tok
  * engram_gather_reduce in direct mode for a batch of n_seq sequences of
  * seq_len tokens whose addresses engram_hash wrote (addr[n_seq*seq_len][48],
  * token-major).  Same results, bitwise; the tokens are visited in tiles of 64
- * positions, sequence by sequence within a tile, so that sequences sharing a
- * prefix read each prefix row from L2 after its first fetch (the pages hash
+ * positions, several sequences at the same position per workgroup, so that
+ * sequences sharing a prefix gather each prefix window once per workgroup
+ * (in a batch of 8,192 tokens or more, tokens with equal addresses share one
+ * gather) and read its rows from L2 after their first fetch (the pages hash
  * every address before the lookup [VRAM; GUIDE "Engram"], and batched prompts
  * often share a system prefix).
  *
@@ -272,10 +274,10 @@ int engram_gather_rows(engram_plan_t plan, const uint32_t* addr, int64_t n_tok, 
  * in one launch, without the address buffer.  The addresses depend on the
  * ids alone [VRAM; GUIDE "Engram"], so each (token, module) computes its own
  * 24 rows and gathers them.  Bitwise identical to the two calls.  A batch
- * of sequences is visited in tiles of 64 positions, sequence by sequence
- * within a tile, so sequences that share a prefix read each prefix row from
- * L2 after its first fetch: passing such sequences in one call is cheaper
- * than one call each.
+ * of sequences is visited in the order of engram_gather_reduce_batched, so
+ * sequences that share a prefix gather each prefix window once per workgroup
+ * and read its rows from L2 after their first fetch: passing such sequences
+ * in one call is cheaper than one call each.
  *
  *   ids, history, n_seq, seq_len   as for engram_hash.
  *   out       device fp32 [n_seq*seq_len][2][256], 16-byte aligned (output).

@@ -20,10 +20,14 @@ def _say(msg):
 
 @pytest.mark.parametrize("fmt", ["f32_row", "e8m0_block32"])
 @pytest.mark.parametrize("n_seq,seq_len,shared", [
-    (1, 1000, 0), (3, 5, 0), (5, 77, 30), (64, 300, 128), (2, 64, 64), (7, 129, 0), (64, 1, 0),
-    # 2 sequences per block, one idle wave; 4 per block, three idle; idle
-    # positions in a narrow tile; every sequence equal
-    (9, 70, 40), (33, 67, 50), (6, 3, 3), (10, 67, 20), (4, 130, 130),
+    (1, 1000, 0), (3, 5, 0), (5, 77, 30), (2, 64, 64), (7, 129, 0), (64, 1, 0),
+    # below 8,192 tokens (no sharing between waves): 2 or 4 sequences per
+    # block with idle waves or idle positions in a narrow tile
+    (9, 70, 40), (33, 67, 50), (6, 3, 3), (10, 67, 20),
+    # 8,192 tokens and more (waves with equal addresses share one gather):
+    # 4 sequences per block; 2 per block with one idle wave; 4 per block with
+    # three idle; idle positions in a narrow last tile; every sequence equal
+    (64, 300, 128), (24, 350, 100), (9, 1000, 400), (33, 260, 100), (10, 835, 300), (4, 2050, 2050),
 ])
 def test_batched_equals_flat(fmt, n_seq, seq_len, shared):
     _say(f"batched gather {n_seq}x{seq_len} shared={shared} {fmt}")
@@ -46,7 +50,7 @@ def test_batched_equals_flat(fmt, n_seq, seq_len, shared):
     assert torch.equal(fused, flat)
 
 
-@pytest.mark.parametrize("n_seq", [8, 10])
+@pytest.mark.parametrize("n_seq", [8, 10, 16])
 def test_batched_partial_sharing_within_blocks(n_seq):
     """Sequences equal to a later, not the first, sequence of their block, and
     equal over part of their length only: every wave must take the sum of the
@@ -55,11 +59,14 @@ def test_batched_partial_sharing_within_blocks(n_seq):
     t, c = small_device_tables(*workloads.dense_tables(32, 4096, "f32_row"))
     plan = lib().Plan(t, c)
     rng = np.random.default_rng(700 + n_seq)
-    ids = rng.integers(0, 129280, size=(n_seq, 150)).astype(np.int32)
+    ids = rng.integers(0, 129280, size=(n_seq, 1100)).astype(np.int32)  # >= 8,192 tokens: sharing on
     ids[2] = ids[1]
-    ids[3, :75] = ids[0, :75]
-    ids[7, 40:] = ids[5, 40:]
+    ids[3, :550] = ids[0, :550]
+    ids[7, 300:] = ids[5, 300:]
     ids[6, ::2] = ids[4, ::2]
+    if n_seq >= 16:
+        ids[15] = ids[9]
+        ids[12, 700:] = ids[0, 700:]
     d_ids, _ = to_dev_ids(ids, None)
     addr = lib().hash(plan, d_ids)
     flat = lib().gather_reduce(plan, addr)
@@ -171,15 +178,17 @@ def test_batch_invariance_of_the_batch_paths(route):
     """A sequence's vectors are bitwise the same whichever sequences share its batch, also on the paths where the
     batch changes the visiting order (tiles of positions across sequences) or the work itself (dedup groups that
     span sequences): the sequence alone, by the flat two calls, against the same sequence as row 4 of a 6-sequence
-    batch whose row 1 shares its first 300 ids and whose row 5 repeats it whole."""
+    batch whose row 1 shares its first 300 ids and whose row 5 repeats it whole.  The batch holds 8,400 tokens,
+    enough for the batch order to share sums between the waves of a block."""
     _say(f"batch invariance through {route}")
     R = 4096
     host_t, host_c = workloads.dense_tables(557, R)
     t, c = small_device_tables(host_t, host_c)
     plan = lib().Plan(t, c, vocab_size=workloads.VOCAB)
     rng = np.random.default_rng(3)
-    a = workloads.zipf_ids(rng, 700).reshape(1, 700)
-    batch = workloads.zipf_ids(rng, 6 * 700).reshape(6, 700)
+    L = 1400
+    a = workloads.zipf_ids(rng, L).reshape(1, L)
+    batch = workloads.zipf_ids(rng, 6 * L).reshape(6, L)
     batch[4] = a[0]
     batch[5] = a[0]
     batch[1, :300] = a[0, :300]
@@ -195,5 +204,5 @@ def test_batch_invariance_of_the_batch_paths(route):
     else:
         lib().gather_reduce(plan, lib().hash(plan, d_ids), out=out, groups=lib().dedup(plan, d_ids))
     torch.cuda.synchronize()
-    assert torch.equal(out[4 * 700:5 * 700], alone)
-    assert torch.equal(out[5 * 700:6 * 700], alone)
+    assert torch.equal(out[4 * L:5 * L], alone)
+    assert torch.equal(out[5 * L:6 * L], alone)
