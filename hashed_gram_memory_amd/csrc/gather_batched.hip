@@ -7,10 +7,11 @@
 // XCD's L2 serve the repeats.  Per token the work, and so the result, is that
 // of gather_reduce_kernel: the same loader and fused multiply-add sequence.
 //
-// With several sequences per block in a large batch (kShare), the 4 waves of a block are the
-// same position of consecutive sequences.  Each posts its 24 addresses in
-// LDS; a wave whose addresses equal an earlier wave's does not gather but
-// takes that wave's sum from LDS after a barrier, since equal addresses give
+// With several sequences per block in a large batch (kShare), the waves of a
+// block that share a position are that position of consecutive sequences.  Each posts its 24 addresses and
+// its token in LDS; after a barrier, a wave whose addresses equal an earlier
+// wave's ends, and the first wave of each set of equal addresses gathers once
+// and stores the sum to every token of the set, since equal addresses give
 // the same rows and so the same sum.  A prefix shared by the batch is then
 // gathered once per block of sequences instead of once per sequence.
 #include "batch_order.h"
@@ -19,8 +20,8 @@
 namespace engram {
 namespace {
 
-template <int FMT, bool kShare>
-__global__ __launch_bounds__(256) void gather_batched_kernel(const GatherParams P, const uint32_t* __restrict__ addr,
+template <int FMT, uint32_t W, bool kShare>
+__global__ __launch_bounds__(64 * W) void gather_batched_kernel(const GatherParams P, const uint32_t* __restrict__ addr,
                                                              uint32_t blk_base, BatchOrder o,
                                                              float* __restrict__ out) {
     const uint32_t module = blockIdx.x & 1u;  // block b: module b % 2 of batch-order block b / 2
@@ -43,36 +44,32 @@ __global__ __launch_bounds__(256) void gather_batched_kernel(const GatherParams 
         __builtin_nontemporal_store(sum_rows<FMT>(r, lane), dst);
         return;
     }
-    __shared__ uint32_t sa[kBlockWaves][kRowsPerModule];
-    __shared__ uint32_t sval[kBlockWaves];
-    __shared__ f32x4 sacc[kBlockWaves][64];
+    __shared__ uint32_t sa[W][kRowsPerModule];
+    __shared__ uint32_t stok[W];  // token + 1; 0 for an idle wave
     const RowBases rb = row_bases(P, s0, lane);
     if (lane < kRowsPerModule) sa[wave][lane] = a;
-    if (lane == 0) sval[wave] = valid ? 1u : 0u;
+    if (lane == 0) stok[wave] = valid ? static_cast<uint32_t>(tok) + 1u : 0u;
     __syncthreads();
-    const uint32_t src = valid ? first_equal_wave(sa, sval, wave, lane, a) : kBlockWaves;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (src == wave) {
-        RowSet r;
-        load_rows_at<FMT>(rb, a, lane, r);
-        acc = sum_rows<FMT>(r, lane);
-        sacc[wave][lane] = acc;
-    }
-    __syncthreads();
-    if (!valid) return;
-    if (src != wave) acc = sacc[src][lane];
+    // The first wave of each set of equal addresses gathers and stores the sum
+    // to every token of the set; the others have nothing left to do.
+    if (!valid || first_equal_wave(sa, stok, wave, lane, a) != wave) return;
+    RowSet r;
+    load_rows_at<FMT>(rb, a, lane, r);
+    const f32x4 acc = sum_rows<FMT>(r, lane);
     __builtin_nontemporal_store(acc, dst);
+    store_to_equal_waves<W>(sa, stok, wave, lane, a, acc, out + module * kRowBytes + lane * 4u);
 }
 
 template <int FMT>
 void launch_one(const GatherParams& p, const uint32_t* addr, uint32_t base, uint32_t nb, const BatchOrder& o,
                 float* out, hipStream_t stream) {
-    if (o.share)
-        hipLaunchKernelGGL((gather_batched_kernel<FMT, true>), dim3(2u * nb), dim3(256), 0, stream, p, addr, base, o,
-                           out);
+    const dim3 grid(2u * nb);
+    if (o.wshift == 3)
+        hipLaunchKernelGGL((gather_batched_kernel<FMT, 8, true>), grid, dim3(512), 0, stream, p, addr, base, o, out);
+    else if (o.share)
+        hipLaunchKernelGGL((gather_batched_kernel<FMT, 4, true>), grid, dim3(256), 0, stream, p, addr, base, o, out);
     else
-        hipLaunchKernelGGL((gather_batched_kernel<FMT, false>), dim3(2u * nb), dim3(256), 0, stream, p, addr, base, o,
-                           out);
+        hipLaunchKernelGGL((gather_batched_kernel<FMT, 4, false>), grid, dim3(256), 0, stream, p, addr, base, o, out);
 }
 
 }  // namespace

@@ -58,8 +58,8 @@ struct Tokens {
 // (kGroups).
 enum { kTokens = 0, kShared = 1, kGroups = 2 };
 
-template <bool POW2, int FMT, int MODE>
-__global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const Tokens T, uint32_t base,
+template <bool POW2, int FMT, int MODE, uint32_t W = kBlockWaves>
+__global__ __launch_bounds__(64 * W) void lookup_kernel(const LookupParams P, const Tokens T, uint32_t base,
                                                      uint32_t item_end, BatchOrder batch, float* __restrict__ out) {
     const int32_t* __restrict__ ids = T.ids;
     const int32_t* __restrict__ history = T.history;
@@ -144,26 +144,20 @@ __global__ __launch_bounds__(256) void lookup_kernel(const LookupParams P, const
 
     const size_t col = static_cast<size_t>(m) * kRowBytes + lane * 4u;
     if (MODE == kShared) {
-        // as gather_batched_kernel: a wave whose 24 addresses equal an earlier
-        // wave's of the block takes that wave's sum instead of gathering
-        __shared__ uint32_t sa[kBlockWaves][kRowsPerModule];
-        __shared__ uint32_t sval[kBlockWaves];
-        __shared__ f32x4 sacc[kBlockWaves][64];
+        // as gather_batched_kernel: the first wave of each set of equal
+        // addresses in the block gathers once and stores to every token of
+        // the set; the others end after the barrier
+        __shared__ uint32_t sa[W][kRowsPerModule];
+        __shared__ uint32_t stok[W];
         if (lane < kRowsPerModule) sa[wave][lane] = a;
-        if (lane == 0) sval[wave] = valid ? 1u : 0u;
+        if (lane == 0) stok[wave] = valid ? tok + 1u : 0u;
         __syncthreads();
-        const uint32_t src = valid ? first_equal_wave(sa, sval, wave, lane, a) : kBlockWaves;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (src == wave) {
-            RowSet r;
-            load_rows_at<FMT>(rb, a, lane, r);
-            acc = sum_rows<FMT>(r, lane);
-            sacc[wave][lane] = acc;
-        }
-        __syncthreads();
-        if (!valid) return;
-        if (src != wave) acc = sacc[src][lane];
+        if (!valid || first_equal_wave(sa, stok, wave, lane, a) != wave) return;
+        RowSet r;
+        load_rows_at<FMT>(rb, a, lane, r);
+        const f32x4 acc = sum_rows<FMT>(r, lane);
         __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + static_cast<size_t>(tok) * (2 * kRowBytes) + col));
+        store_to_equal_waves<W>(sa, stok, wave, lane, a, acc, out + col);
         return;
     }
     RowSet r;
@@ -198,6 +192,9 @@ void launch_one(const LookupParams& p, const Tokens& tk, uint32_t grid, uint32_t
                 const BatchOrder& batch, float* out, hipStream_t stream) {
     if (tk.perm)
         hipLaunchKernelGGL((lookup_kernel<POW2, FMT, kGroups>), dim3(grid), dim3(256), 0, stream, p, tk, base, end,
+                           batch, out);
+    else if (batch.wshift == 3)
+        hipLaunchKernelGGL((lookup_kernel<POW2, FMT, kShared, 8>), dim3(grid), dim3(512), 0, stream, p, tk, base, end,
                            batch, out);
     else if (batch.share)
         hipLaunchKernelGGL((lookup_kernel<POW2, FMT, kShared>), dim3(grid), dim3(256), 0, stream, p, tk, base, end,

@@ -25,9 +25,11 @@ def _say(msg):
     # block with idle waves or idle positions in a narrow tile
     (9, 70, 40), (33, 67, 50), (6, 3, 3), (10, 67, 20),
     # 8,192 tokens and more (waves with equal addresses share one gather):
-    # 4 sequences per block; 2 per block with one idle wave; 4 per block with
-    # three idle; idle positions in a narrow last tile; every sequence equal
-    (64, 300, 128), (24, 350, 100), (9, 1000, 400), (33, 260, 100), (10, 835, 300), (4, 2050, 2050),
+    # 8 sequences per block (8-wave blocks); 8 per block with seven idle
+    # waves; 2 per block with one idle; 4 per block with three idle; idle
+    # positions in a narrow last tile; every sequence equal
+    (64, 300, 128), (24, 350, 100), (57, 150, 60), (9, 1000, 400), (33, 260, 100), (10, 835, 300),
+    (4, 2050, 2050),
 ])
 def test_batched_equals_flat(fmt, n_seq, seq_len, shared):
     _say(f"batched gather {n_seq}x{seq_len} shared={shared} {fmt}")
