@@ -228,7 +228,7 @@ int engram_gather_reduce(engram_plan_t plan, const uint32_t* addr, int64_t n_tok
  * engram_gather_reduce in direct mode for a batch of n_seq sequences of
  * seq_len tokens whose addresses engram_hash wrote (addr[n_seq*seq_len][48],
  * token-major).  Same results, bitwise; the tokens are visited in tiles of 64
- * positions, several sequences at the same position per workgroup, so that
+ * positions, up to 8 sequences at the same position per workgroup, so that
  * sequences sharing a prefix gather each prefix window once per workgroup
  * (in a batch of 8,192 tokens or more, tokens with equal addresses share one
  * gather) and read its rows from L2 after their first fetch (the pages hash
