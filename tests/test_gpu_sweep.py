@@ -1,7 +1,9 @@
 """A seeded sweep over the lookup paths against the oracle.  Each case draws a batch shape, row counts per
 sub-table (powers of two, one odd count, or a mix that includes 1-row sub-tables), a scale format, history or
 none, a vocabulary map or none, a hash seed and an id range (from a handful of ids, so windows repeat, to the
-whole vocabulary).  Every token's addresses must equal the oracle's bit for bit, and every memory vector must lie
+whole vocabulary).  Cases 16 and up are batches of 8,192 tokens or more, where the batch-order paths share one
+gather among the waves of a block with equal addresses; their sequences also share a prefix of random length.
+Every token's addresses must equal the oracle's bit for bit, and every memory vector must lie
 within 1e-5 x sum|terms| of the oracle, through every path that computes it: engram_hash + engram_gather_reduce,
 engram_lookup, engram_gather_reduce_batched, and the dedup-mode gather and lookup over engram_dedup's groups.
 The paths share one summation order, so they must also agree with each other bitwise."""
@@ -44,11 +46,16 @@ def _tables(seed, rows, fmt):
     return host_t, host_c, dev_t, dev_c
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(24))
 def test_lookup_paths_random_cases(case):
     rng = np.random.default_rng(7000 + case)
-    n_seq = int(rng.integers(1, 9))
-    seq_len = int(rng.integers(1, 400))
+    large = case >= 16
+    if large:
+        n_seq = int((8, 12, 16, 24, 57, 64, 9, 33)[case - 16])
+        seq_len = -(-int(rng.integers(8192, 12000)) // n_seq)
+    else:
+        n_seq = int(rng.integers(1, 9))
+        seq_len = int(rng.integers(1, 400))
     fmt = ("f32_row", "e8m0_block32")[case % 2]
     rows = _rows((case // 2) % 4, rng)
     with_hist = bool(rng.integers(0, 2))
@@ -60,6 +67,9 @@ def test_lookup_paths_random_cases(case):
         hi = min(hi, workloads.VOCAB)
     _say(f"sweep case {case}: {n_seq}x{seq_len} {fmt} rows[0]={rows[0]} hist={with_hist} map={use_map} ids<{hi}")
     ids = rng.integers(0, hi, size=(n_seq, seq_len), dtype=np.int64).astype(np.int32)
+    if large:  # every sequence starts with the first one's prefix
+        prefix = int(rng.integers(0, seq_len + 1))
+        ids[:, :prefix] = ids[0, :prefix]
     hist = rng.integers(0, hi, size=(n_seq, 3), dtype=np.int64).astype(np.int32) if with_hist else None
     vmap = workloads.vocab_map(100 + case) if use_map else None
 
