@@ -77,8 +77,8 @@ inline BatchOrder batch_order(uint32_t n_tok, uint32_t seq_len) {
 // Sequence and position of wave `wave` of block `blk` (< o.n_blocks); *valid
 // is false for the idle waves of a partial group or a narrow last tile.
 // Host-callable too, so the mapping can be checked on the CPU.
-__host__ __device__ __forceinline__ void block_token(uint32_t blk, uint32_t wave, const BatchOrder& o, uint32_t* seq,
-                                            uint32_t* t, bool* valid) {
+__host__ __device__ __forceinline__ void block_token(uint32_t blk, uint32_t wave, const BatchOrder& o,
+                                                     uint32_t* seq, uint32_t* t, bool* valid) {
     uint32_t tile_idx = o.full_tiles, rem, width = o.last;
     if (blk < o.full_tiles * o.tile_blocks) {
         tile_idx = blk / o.tile_blocks;

@@ -8,12 +8,13 @@
 // of gather_reduce_kernel: the same loader and fused multiply-add sequence.
 //
 // With several sequences per block in a large batch (kShare), the waves of a
-// block that share a position are that position of consecutive sequences.  Each posts its 24 addresses and
-// its token in LDS; after a barrier, a wave whose addresses equal an earlier
-// wave's ends, and the first wave of each set of equal addresses gathers once
-// and stores the sum to every token of the set, since equal addresses give
-// the same rows and so the same sum.  A prefix shared by the batch is then
-// gathered once per block of sequences instead of once per sequence.
+// block that share a position are that position of consecutive sequences.
+// Each wave posts its 24 addresses and its token in LDS; after a barrier, a
+// wave whose addresses equal an earlier wave's ends, and the first wave of
+// each set of equal addresses gathers once and stores the sum to every token
+// of the set, since equal addresses give the same rows and so the same sum.
+// A prefix shared by the batch is then gathered once per block of sequences
+// instead of once per sequence.
 #include "batch_order.h"
 #include "row_sum.h"
 
@@ -21,9 +22,9 @@ namespace engram {
 namespace {
 
 template <int FMT, uint32_t W, bool kShare>
-__global__ __launch_bounds__(64 * W) void gather_batched_kernel(const GatherParams P, const uint32_t* __restrict__ addr,
-                                                             uint32_t blk_base, BatchOrder o,
-                                                             float* __restrict__ out) {
+__global__ __launch_bounds__(64 * W) void gather_batched_kernel(const GatherParams P,
+                                                                const uint32_t* __restrict__ addr, uint32_t blk_base,
+                                                                BatchOrder o, float* __restrict__ out) {
     const uint32_t module = blockIdx.x & 1u;  // block b: module b % 2 of batch-order block b / 2
     const uint32_t blk = blk_base + (blockIdx.x >> 1);
     if (blk >= o.n_blocks) return;  // the whole block

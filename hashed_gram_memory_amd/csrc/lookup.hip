@@ -9,9 +9,10 @@
 // which is what a decode step of a few tokens is made of.
 //
 // Mapping: one wave per (token, module), tokens visited in the batch order
-// of batch_order.h (tiles of 64 positions, sequence by sequence within a
-// tile; plain token order for one sequence).  The window ids are
-// wave-uniform; lane q < 24
+// of batch_order.h (tiles of 64 positions, several sequences at the same
+// position per block; plain token order for one sequence).  In a large batch
+// the waves of a block with equal addresses share one gather, as in the
+// batched gather.  The window ids are wave-uniform; lane q < 24
 // hashes row q of the module in parallel with the others, with the same
 // multiply-xor and modulus (a mask for power-of-two row counts) as
 // hash_kernel, and then owns that row in the lane-addressed loads.  The
@@ -53,14 +54,14 @@ struct Tokens {
 };
 
 // How a launch maps blocks to tokens: the batch order of batch_order.h,
-// each wave gathering for itself (kTokens) or waves with equal addresses
-// sharing one gather through LDS (kShared); or one wave per dedup group
-// (kGroups).
+// each wave gathering for itself (kTokens) or the waves posting their
+// addresses in LDS and the first of each set of equal ones gathering for all
+// (kShared); or one wave per dedup group (kGroups).
 enum { kTokens = 0, kShared = 1, kGroups = 2 };
 
 template <bool POW2, int FMT, int MODE, uint32_t W = kBlockWaves>
 __global__ __launch_bounds__(64 * W) void lookup_kernel(const LookupParams P, const Tokens T, uint32_t base,
-                                                     uint32_t item_end, BatchOrder batch, float* __restrict__ out) {
+                                                        uint32_t item_end, BatchOrder batch, float* __restrict__ out) {
     const int32_t* __restrict__ ids = T.ids;
     const int32_t* __restrict__ history = T.history;
     const uint32_t m = blockIdx.x & 1u;  // block b: module b % 2
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(64 * W) void lookup_kernel(const LookupParams P, co
     const uint32_t lane = threadIdx.x & 63u;
 
     uint32_t item = 0;  // kGroups: the group
-    bool valid = true;  // kShared: an idle wave of a partial block still takes part in its barriers
+    bool valid = true;  // kShared: an idle wave of a partial block still takes part in its barrier
     uint32_t seq = 0, t = 0;
     if (MODE == kGroups) {
         item = base + (blockIdx.x >> 1) * kBlockWaves + wave;
