@@ -208,3 +208,54 @@ def test_batch_invariance_of_the_batch_paths(route):
     torch.cuda.synchronize()
     assert torch.equal(out[4 * L:5 * L], alone)
     assert torch.equal(out[5 * L:6 * L], alone)
+
+
+def test_sharing_paths_graph_replay_matches_eager():
+    """hash + engram_gather_reduce_batched + engram_lookup on a 16 x 640 batch (10,240 tokens: 8 sequences per
+    block, waves with equal addresses share one gather) capture into one HIP graph; each replay, on new ids with a
+    shared prefix of a new length, matches the eager flat gather bitwise and the oracle within tolerance."""
+    _say("batch-order sharing paths in a hip graph")
+    n_seq, seq_len, R = 16, 640, 4096
+    host_t, host_c = workloads.dense_tables(33, R)
+    t, c = small_device_tables(host_t, host_c)
+    plan = lib().Plan(t, c)
+    rng = np.random.default_rng(34)
+
+    def draw():
+        ids = workloads.zipf_ids(rng, n_seq * seq_len).reshape(n_seq, seq_len)
+        prefix = int(rng.integers(0, seq_len + 1))
+        ids[:, :prefix] = ids[0, :prefix]
+        return ids
+
+    ids = draw()
+    d_ids, _ = to_dev_ids(ids, None)
+    n_tok = n_seq * seq_len
+    addr = torch.empty((n_tok, 48), dtype=torch.uint32, device="cuda")
+    out_b = torch.empty((n_tok, 2, 256), dtype=torch.float32, device="cuda")
+    out_f = torch.empty_like(out_b)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up on the side stream, as capture requires
+        lib().hash(plan, d_ids, out=addr)
+        lib().gather_reduce_batched(plan, addr, n_seq, out=out_b)
+        lib().lookup(plan, d_ids, out=out_f)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib().hash(plan, d_ids, out=addr)
+        lib().gather_reduce_batched(plan, addr, n_seq, out=out_b)
+        lib().lookup(plan, d_ids, out=out_f)
+    for rep in range(4):
+        ids = draw()
+        d_ids.copy_(torch.from_numpy(ids))
+        out_b.fill_(float("nan"))
+        out_f.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        eager = lib().gather_reduce(plan, lib().hash(plan, d_ids))
+        torch.cuda.synchronize()
+        assert torch.equal(out_b, eager), rep
+        assert torch.equal(out_f, eager), rep
+        sample = np.concatenate([np.arange(0, 70), rng.integers(0, n_tok, size=400), np.arange(n_tok - 70, n_tok)])
+        _, want, abs_sum = oracle.lookup(ids, None, host_t, host_c, [R] * 48)
+        assert_within_tolerance(out_b.cpu().numpy()[sample], want[sample], abs_sum[sample])
