@@ -63,7 +63,8 @@ int main() {
             if (check(n_seq, len)) return 1;
             ++shapes;
         }
-    const uint32_t big[][2] = {{64, 8192}, {57, 150}, {9, 1000}, {33, 260}, {128, 96}, {200, 41}, {1, 131072}};
+    const uint32_t big[][2] = {{64, 8192}, {57, 150}, {9, 1000}, {33, 260}, {128, 96}, {200, 41}, {1, 131072},
+                               {8200, 1}, {4100, 2}, {2731, 3}};
     for (const auto& b : big) {
         if (check(b[0], b[1])) return 1;
         ++shapes;

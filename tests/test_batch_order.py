@@ -1,6 +1,6 @@
 """The batch order of the batched gather and the fused lookup, checked on the CPU: tests/batch_order_check.cpp is
 compiled against the library's own header (batch_order.h) and enumerates the token of every wave of every block
-for 1,447 batch shapes (1 to 80 sequences of 18 lengths, and a few large ones): every token is visited exactly once
+for 1,450 batch shapes (1 to 80 sequences of 18 lengths, and a few large ones): every token is visited exactly once
 and in bounds, blocks are 4 or 8 waves with 8 only where waves share gathers, and consecutive sequence groups of a
 full tile are a multiple of 8 launch slots apart.  No GPU is used: block_token is host-callable."""
 import os

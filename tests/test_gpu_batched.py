@@ -259,3 +259,32 @@ def test_sharing_paths_graph_replay_matches_eager():
         sample = np.concatenate([np.arange(0, 70), rng.integers(0, n_tok, size=400), np.arange(n_tok - 70, n_tok)])
         _, want, abs_sum = oracle.lookup(ids, None, host_t, host_c, [R] * 48)
         assert_within_tolerance(out_b.cpu().numpy()[sample], want[sample], abs_sum[sample])
+
+
+@pytest.mark.parametrize("n_seq,seq_len", [(8200, 1), (4100, 2), (2731, 3)])
+def test_sharing_with_history_windows(n_seq, seq_len):
+    """Large batches of very short sequences (a big decode or speculative step): every window reads the caller's
+    history, and the batch holds 8,192 tokens or more, so waves with equal addresses share one gather.  Ids and
+    histories come from a few values and repeat, so many windows are equal.  The batch-order gather and the fused
+    lookup must equal the flat gather bitwise and the oracle within tolerance on every token."""
+    _say(f"sharing with history windows, {n_seq} x {seq_len}")
+    R = 4096
+    host_t, host_c = workloads.dense_tables(35, R)
+    t, c = small_device_tables(host_t, host_c)
+    plan = lib().Plan(t, c)
+    rng = np.random.default_rng(36 + seq_len)
+    ids = rng.integers(0, 5, size=(n_seq, seq_len)).astype(np.int32)
+    hist = rng.integers(0, 5, size=(n_seq, 3)).astype(np.int32)
+    d_ids, d_hist = to_dev_ids(ids, hist)
+    addr = lib().hash(plan, d_ids, d_hist)
+    flat = lib().gather_reduce(plan, addr)
+    batched = torch.full_like(flat, float("nan"))
+    lib().gather_reduce_batched(plan, addr, n_seq, out=batched)
+    fused = torch.full_like(flat, float("nan"))
+    lib().lookup(plan, d_ids, d_hist, out=fused)
+    torch.cuda.synchronize()
+    assert torch.equal(batched, flat)
+    assert torch.equal(fused, flat)
+    want_addr, want, abs_sum = oracle.lookup(ids, hist, host_t, host_c, [R] * 48)
+    assert np.array_equal(addr_to_host(addr), want_addr)
+    assert_within_tolerance(flat.cpu().numpy(), want, abs_sum)
