@@ -179,7 +179,8 @@ def test_batched_order_across_the_chunk_boundary():
 
 
 def test_one_plan_on_two_streams():
-    """A plan is immutable: concurrent calls on two streams give the sequential results."""
+    """A plan is immutable: concurrent calls on two streams give the sequential results (the 4 x 3,000-token
+    batches are large enough for the batch-order paths to share gathers within a block)."""
     _say("one plan, two streams")
     R = 4096
     host_t, host_c = workloads.dense_tables(10, R)
@@ -194,6 +195,7 @@ def test_one_plan_on_two_streams():
     outs = [torch.empty_like(want[0]) for _ in range(2)]
     fused = [torch.empty_like(want[0]) for _ in range(2)]
     groups_out = [torch.empty_like(want[0]) for _ in range(2)]
+    batched_out = [torch.empty_like(want[0]) for _ in range(2)]
     for rep in range(3):
         for i, s in enumerate(streams):
             s.wait_stream(torch.cuda.current_stream())
@@ -203,8 +205,10 @@ def test_one_plan_on_two_streams():
                 lib().lookup(plan, d[i], out=fused[i], stream=s)
                 g = lib().dedup(plan, d[i], stream=s)
                 lib().gather_reduce(plan, a, out=groups_out[i], groups=g, stream=s)
+                lib().gather_reduce_batched(plan, a, 4, out=batched_out[i], stream=s)
         torch.cuda.synchronize()
         for i in range(2):
             assert torch.equal(outs[i], want[i]), (rep, i)
             assert torch.equal(fused[i], want[i]), (rep, i)
             assert torch.equal(groups_out[i], want[i]), (rep, i)
+            assert torch.equal(batched_out[i], want[i]), (rep, i)
