@@ -24,7 +24,8 @@
 //   * cache policy by n-gram order: the order-2 rows, which a token stream
 //     repeats, are plain loads that L2 may keep; the order-3 and order-4
 //     rows, nearly all read once, are non-temporal (every 4-byte scale read
-//     still fetches a whole 128-byte line on gfx950);
+//     still fetches a 64-byte sector: scalar-cache misses leave L2 as
+//     64-byte requests);
 //   * decode with the gfx950 packed FP8 (OCP E4M3) -> fp32 conversion, then
 //     fused multiply-add into 4 fp32 accumulators per lane in ascending q
 //     (row_sum.h, shared with the fused lookup);
