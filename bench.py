@@ -45,17 +45,22 @@ WORKLOAD_TEXT = {
     5: ("batched prefill with shared prefixes: 64 x (4096 shared + 4096 own) Zipf(1.1) ids over 129280; 48 "
         "sub-tables x 2^24 rows x 256 B FP8 E4M3 (192 GiB) + fp32 row scales"),
 }
-PMC_FILE = os.path.join(ROOT, "profiles", "gather_reduce_full_131072_pmc.json")
-# sources the gather kernel is compiled from (the counter summary is valid only for this exact code)
-GATHER_SRCS = [os.path.join(ROOT, "hashed_gram_memory_amd", "csrc", f)
-               for f in ("gather_reduce.hip", "row_sum.h", "engram_internal.h")]
+CSRC = os.path.join(ROOT, "hashed_gram_memory_amd", "csrc")
+# Counter summaries of the timed gather kernel, per workload, each valid only for the exact code it was taken on:
+# the file and the sources that kernel is compiled from.
+PMC_RECORDS = {
+    4: (os.path.join(ROOT, "profiles", "gather_reduce_full_131072_pmc.json"),
+        [os.path.join(CSRC, f) for f in ("gather_reduce.hip", "row_sum.h", "engram_internal.h")]),
+    5: (os.path.join(ROOT, "profiles", "gather_batched_524288_pmc.json"),
+        [os.path.join(CSRC, f) for f in ("gather_batched.hip", "batch_order.h", "row_sum.h", "engram_internal.h")]),
+}
 
 
-def gather_source_sha256() -> str:
-    """sha256 of the gather kernel's code: its sources with // comments, blank lines and indentation removed,
-    so that editing a comment does not detach the stored counters from the kernel they were taken on."""
+def source_sha256(srcs) -> str:
+    """sha256 of a kernel's code: its sources with // comments, blank lines and indentation removed, so that
+    editing a comment does not detach the stored counters from the kernel they were taken on."""
     h = hashlib.sha256()
-    for f in GATHER_SRCS:
+    for f in srcs:
         for line in open(f, encoding="utf-8"):
             code = line.split("//", 1)[0].strip()
             if code:
@@ -63,28 +68,41 @@ def gather_source_sha256() -> str:
     return h.hexdigest()
 
 
+def gather_source_sha256() -> str:
+    """The code hash of the flat gather (workload 4's timed kernel)."""
+    return source_sha256(PMC_RECORDS[4][1])
+
+
 def _log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def _traffic(n_tok: int, id_batches: int):
-    """HBM bytes per gather launch from the committed counter summary, if it matches the current kernel and run."""
+def _pmc_record(workload: int, n_tok: int, id_batches: int):
+    """The committed counter summary of this workload's gather, if it matches the current kernel and run."""
+    if workload not in PMC_RECORDS:
+        return None
+    path, srcs = PMC_RECORDS[workload]
     try:
-        rec = json.load(open(PMC_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if (rec.get("kernel_source_sha256") != gather_source_sha256() or rec.get("n_tok") != n_tok
+    if (rec.get("kernel_source_sha256") != source_sha256(srcs) or rec.get("n_tok") != n_tok
             or rec.get("id_batches") != id_batches):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
-def _traffic_exact(n_tok: int, id_batches: int):
-    """Bytes per gather launch leaving L2 from the request-size counters (128- and 64-byte reads, 64-byte writes),
-    under the same kernel and run checks as the FETCH_SIZE/WRITE_SIZE figure."""
-    if _traffic(n_tok, id_batches) is None:
-        return None
-    return json.load(open(PMC_FILE)).get("request_sizes", {}).get("bytes_exact")
+def _traffic(workload: int, n_tok: int, id_batches: int):
+    """HBM bytes per gather launch from FETCH_SIZE and WRITE_SIZE scaled by the copy calibration, when recorded."""
+    rec = _pmc_record(workload, n_tok, id_batches)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
+
+
+def _traffic_exact(workload: int, n_tok: int, id_batches: int):
+    """Bytes per gather launch leaving L2 from the request-size counters (128- and 64-byte reads) and WRITE_SIZE,
+    under the same kernel and run checks."""
+    rec = _pmc_record(workload, n_tok, id_batches)
+    return None if rec is None else rec.get("request_sizes", {}).get("bytes_exact")
 
 
 def _oracle_worker(pieces, rows: int, seed: int, dense: bool, barrier, queue) -> None:
@@ -631,8 +649,8 @@ def main(argv=None) -> int:
         gather_bytes = (GATHER_BYTES_PER_TOKEN - 48 * 4 + scale_bytes) * n_tok
     achieved = gather_bytes / (gather_ms / 1e3) / 1e9
     plain = not (args.dedup or mx or args.vocab_map or args.prime_rows or args.uniform_ids or args.flush_mib)
-    traffic_fetch = _traffic(n_tok, args.id_batches) if args.workload == 4 and plain else None
-    traffic = _traffic_exact(n_tok, args.id_batches) if args.workload == 4 and plain else None
+    traffic_fetch = _traffic(args.workload, n_tok, args.id_batches) if plain else None
+    traffic = _traffic_exact(args.workload, n_tok, args.id_batches) if plain else None
 
     base = None
     if args.cpu_sample > 0 and args.workload == 4:
