@@ -49,10 +49,13 @@ CSRC = os.path.join(ROOT, "hashed_gram_memory_amd", "csrc")
 # Counter summaries of the timed gather kernel, per workload, each valid only for the exact code it was taken on:
 # the file and the sources that kernel is compiled from.
 PMC_RECORDS = {
-    4: (os.path.join(ROOT, "profiles", "gather_reduce_full_131072_pmc.json"),
-        [os.path.join(CSRC, f) for f in ("gather_reduce.hip", "row_sum.h", "engram_internal.h")]),
-    5: (os.path.join(ROOT, "profiles", "gather_batched_524288_pmc.json"),
-        [os.path.join(CSRC, f) for f in ("gather_batched.hip", "batch_order.h", "row_sum.h", "engram_internal.h")]),
+    (4, "direct"): (os.path.join(ROOT, "profiles", "gather_reduce_full_131072_pmc.json"),
+                    [os.path.join(CSRC, f) for f in ("gather_reduce.hip", "row_sum.h", "engram_internal.h")]),
+    (5, "direct"): (os.path.join(ROOT, "profiles", "gather_batched_524288_pmc.json"),
+                    [os.path.join(CSRC, f) for f in ("gather_batched.hip", "batch_order.h", "row_sum.h",
+                                                     "engram_internal.h")]),
+    (5, "dedup"): (os.path.join(ROOT, "profiles", "lookup_dedup_524288_pmc.json"),
+                   [os.path.join(CSRC, f) for f in ("lookup.hip", "batch_order.h", "row_sum.h", "engram_internal.h")]),
 }
 
 
@@ -70,18 +73,19 @@ def source_sha256(srcs) -> str:
 
 def gather_source_sha256() -> str:
     """The code hash of the flat gather (workload 4's timed kernel)."""
-    return source_sha256(PMC_RECORDS[4][1])
+    return source_sha256(PMC_RECORDS[(4, "direct")][1])
 
 
 def _log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def _pmc_record(workload: int, n_tok: int, id_batches: int):
-    """The committed counter summary of this workload's gather, if it matches the current kernel and run."""
-    if workload not in PMC_RECORDS:
+def _pmc_record(key, n_tok: int, id_batches: int):
+    """The committed counter summary of the timed kernel of (workload, step kind), if it matches the current kernel
+    and run."""
+    if key not in PMC_RECORDS:
         return None
-    path, srcs = PMC_RECORDS[workload]
+    path, srcs = PMC_RECORDS[key]
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
@@ -92,16 +96,16 @@ def _pmc_record(workload: int, n_tok: int, id_batches: int):
     return rec
 
 
-def _traffic(workload: int, n_tok: int, id_batches: int):
-    """HBM bytes per gather launch from FETCH_SIZE and WRITE_SIZE scaled by the copy calibration, when recorded."""
-    rec = _pmc_record(workload, n_tok, id_batches)
+def _traffic(key, n_tok: int, id_batches: int):
+    """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE scaled by the copy calibration, when recorded."""
+    rec = _pmc_record(key, n_tok, id_batches)
     return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
-def _traffic_exact(workload: int, n_tok: int, id_batches: int):
-    """Bytes per gather launch leaving L2 from the request-size counters (128- and 64-byte reads) and WRITE_SIZE,
-    under the same kernel and run checks."""
-    rec = _pmc_record(workload, n_tok, id_batches)
+def _traffic_exact(key, n_tok: int, id_batches: int):
+    """Bytes per launch leaving L2 from the request-size counters (128- and 64-byte reads) and WRITE_SIZE, under the
+    same kernel and run checks."""
+    rec = _pmc_record(key, n_tok, id_batches)
     return None if rec is None else rec.get("request_sizes", {}).get("bytes_exact")
 
 
@@ -648,9 +652,11 @@ def main(argv=None) -> int:
     else:
         gather_bytes = (GATHER_BYTES_PER_TOKEN - 48 * 4 + scale_bytes) * n_tok
     achieved = gather_bytes / (gather_ms / 1e3) / 1e9
-    plain = not (args.dedup or mx or args.vocab_map or args.prime_rows or args.uniform_ids or args.flush_mib)
-    traffic_fetch = _traffic(args.workload, n_tok, args.id_batches) if plain else None
-    traffic = _traffic_exact(args.workload, n_tok, args.id_batches) if plain else None
+    plain = not (mx or args.vocab_map or args.prime_rows or args.uniform_ids or args.flush_mib
+                 or (args.dedup and not fused_dedup))
+    pmc_key = (args.workload, "dedup" if fused_dedup else "direct")
+    traffic_fetch = _traffic(pmc_key, n_tok, args.id_batches) if plain else None
+    traffic = _traffic_exact(pmc_key, n_tok, args.id_batches) if plain else None
 
     base = None
     if args.cpu_sample > 0 and args.workload == 4:
